@@ -1,0 +1,196 @@
+/*
+ * dsa_decode.h — C ABI of the MI355X (gfx950) selected-index NoPE MLA paged
+ * decode.
+ *
+ * What it computes, per query row r and local head h (pages cited by title):
+ *   [attend]   page "spark_model/layers/glm5next_dsa/attend.rs"
+ *   [decode_k] page "metrale_model_arch/glm5next_dsa/layer/decode_k.rs"
+ *   [build]    page "spark_model/layers/glm5next_dsa/build.rs"
+ *
+ *   S_r   = the SET of ids t in sel_indices[r, :] with 0 <= t < seq_lens[r]
+ *           ([attend] module doc, "Why this is not the masked kernel": the
+ *           gather is exactly dense attention under a set-membership mask;
+ *           -1 is a hole and repeats collapse). Negative ids are holes; ids
+ *           at or past seq_lens[r] are dropped.
+ *   row_t = the kv_lora_rank FP8 E4M3FN bytes of token t, found through the
+ *           block table ([decode_k] slot computation: page =
+ *           block_tables[r*stride + t/block_size], byte offset =
+ *           page*cache_stride_bytes + (t % block_size)*kv_lora_rank).
+ *   s_t   = sm_scale * k_scale * sum_d q[r,h,d] * fp8(row_t[d])
+ *   out[r,h,:] = v_scale * sum_t softmax(s)_t * fp8(vrow_t[:])   (0 if S_r is empty)
+ *           where vrow_t is read from v_cache at row_t's offset ([attend]
+ *           DsaDecodeInputs: K and V are one latent buffer in absorbed NoPE
+ *           MLA; both pointers are taken). The output stays in the latent
+ *           space ([build] o_absorb consumes [heads, kv_lora_rank]).
+ *
+ * Every function returns DSA_DECODE_OK (0) or a negative status; the reason,
+ * with the offending values, is then available from dsa_decode_last_error()
+ * (thread-local). Nothing falls back to another code path: an unsupported
+ * shape or device is an error ([attend] Glm5NextDsaDecodeKernel::resolve).
+ */
+#ifndef DSA_DECODE_H
+#define DSA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_DECODE_OK 0
+#define DSA_DECODE_ERR_INVALID (-1)     /* bad geometry, pointer or size */
+#define DSA_DECODE_ERR_UNSUPPORTED (-2) /* kv_lora_rank not compiled in */
+#define DSA_DECODE_ERR_DEVICE (-3)      /* no device, or it is not gfx950 */
+#define DSA_DECODE_ERR_WORKSPACE (-4)   /* workspace null, misaligned or small */
+#define DSA_DECODE_ERR_LAUNCH (-5)      /* the HIP runtime refused a launch */
+
+/* Geometry of one decode. All counts are elements unless named _bytes. */
+typedef struct dsa_decode_params {
+  /* Query rows. One row per decoded sequence; q, out, seq_lens and the
+   * selection all have this many rows ([attend] decode_attention refuses a
+   * selection whose row count differs from the sequence count). */
+  int32_t num_rows;
+  /* Local query heads (this tensor-parallel rank's heads). > 0. */
+  int32_t num_q_heads;
+  /* Latent KV heads. Must be 1: MLA keeps a single latent head
+   * ([attend] DsaDecodePaging::validate). */
+  int32_t num_kv_heads;
+  /* D, the latent width and the FP8 bytes per cached token. Supported:
+   * 64, 128, 256, 512. Anything else is DSA_DECODE_ERR_UNSUPPORTED, never
+   * a silent mis-tiling ([attend] decode_attention's kv_lora_rank guard). */
+  int32_t kv_lora_rank;
+  /* Tokens per cache page. > 0. */
+  int32_t block_size;
+  /* The selector's pool width. > 0, and block_size % index_kpool == 0 so a
+   * pool never straddles two pages ([attend] DsaDecodePaging::validate). */
+  int32_t index_kpool;
+  /* W: ids per selection row. > 0. */
+  int32_t sel_width;
+  /* Entries between consecutive rows of block_tables; 0 = every row reads
+   * row 0's table ([decode_k] the attend's block-table row stride). */
+  int32_t block_table_stride;
+  /* Bytes between consecutive pages of the cache; 0 selects
+   * block_size * kv_lora_rank. Must be >= block_size * kv_lora_rank and a
+   * multiple of 16. */
+  uint64_t cache_stride_bytes;
+  /* Upper bound on every seq_lens[r]; > 0. When block_table_stride > 0 it
+   * must not exceed block_table_stride * block_size (a table row must cover
+   * every position it can be asked for: [decode_k] block-table capacity
+   * check). Ids are clamped to it, so a larger seq_lens[r] cannot make the
+   * library read past a table row. */
+  int32_t max_seq_len;
+  /* Softmax scale applied to q . k (explicit; [attend] passes
+   * kv_lora_rank^-0.5, the GLM-5.3 configurations use qk_head_dim^-0.5). */
+  float sm_scale;
+  /* 0: the planner picks how many selected tokens one workgroup handles.
+   * Otherwise a positive multiple of 64 that forces that split (used to test
+   * that the result does not depend on the split). */
+  int32_t chunk_tokens;
+  int32_t reserved[4]; /* must be zero */
+} dsa_decode_params;
+
+/* Opaque plan: validated geometry plus the launch decomposition. Host
+ * memory owned by the library; free it with dsa_decode_plan_destroy. */
+typedef struct dsa_decode_plan_s* dsa_decode_plan_t;
+
+/* Read-only description of a plan. */
+typedef struct dsa_decode_plan_info {
+  int32_t device;          /* HIP device id, or -1 for a host-only plan */
+  int32_t chunk_tokens;    /* selected tokens per attend workgroup */
+  int32_t chunks_per_row;  /* workgroups per row per head block */
+  int32_t head_blocks;     /* groups of up to 64 heads */
+  int32_t attend_workgroups;
+  int32_t uses_combine;    /* 1 when chunks_per_row > 1 */
+  int32_t num_cus;         /* compute units the plan was sized for */
+  int32_t reserved;
+  uint64_t workspace_bytes;
+} dsa_decode_plan_info;
+
+/* Validate params and build a plan.
+ *   params  host pointer, read only, not retained.
+ *   device  HIP device the plan launches on; the device must be gfx950.
+ *           Pass -1 for a host-only plan (validation and sizing without a
+ *           GPU); such a plan cannot be launched.
+ *   out     receives the plan on success, NULL on failure.
+ * Errors: DSA_DECODE_ERR_INVALID for any geometry rule above,
+ * DSA_DECODE_ERR_UNSUPPORTED for kv_lora_rank, DSA_DECODE_ERR_DEVICE when
+ * the device is missing or not gfx950. */
+int dsa_decode_plan(const dsa_decode_params* params, int device,
+                    dsa_decode_plan_t* out);
+
+/* Free a plan (NULL is ignored). */
+void dsa_decode_plan_destroy(dsa_decode_plan_t plan);
+
+/* Device scratch bytes dsa_decode_launch needs (selection ids, token byte
+ * offsets, per-row counts, and split partials when chunks_per_row > 1).
+ * The caller allocates it; 0 for a NULL plan. */
+size_t dsa_decode_workspace_bytes(dsa_decode_plan_t plan);
+
+/* Fill *info. DSA_DECODE_ERR_INVALID for a NULL argument. */
+int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info);
+
+/* Enqueue the decode on `stream` (a hipStream_t; NULL = the default stream).
+ * Asynchronous: nothing is synchronised, nothing is allocated, and nothing is
+ * retained after return ([attend] decode_attention enqueues without
+ * synchronising; DsaDecodeInputs are caller-owned).
+ * Device pointers, all caller-owned:
+ *   q            bf16  [num_rows, num_q_heads, kv_lora_rank], 16-byte aligned
+ *   k_cache      FP8 E4M3FN pool; token rows as described above; 16-byte aligned
+ *   v_cache      same layout as k_cache (may equal it); 16-byte aligned
+ *   block_tables int32 [num_rows or 1, block_table_stride or as needed]
+ *   seq_lens     int32 [num_rows]
+ *   sel_indices  int32 [num_rows, sel_width]
+ *   out          bf16  [num_rows, num_q_heads, kv_lora_rank], 16-byte aligned
+ *   workspace    >= dsa_decode_workspace_bytes(plan) bytes, 256-byte aligned;
+ *                overwritten; must not be shared by launches in flight.
+ * k_scale, v_scale: per-tensor dequantisation scales (finite).
+ * Device-side preconditions (not checked by the kernels): every page id a
+ * selected token maps to lies inside the pool; with block_table_stride 0 the
+ * shared table has an entry for every position < max_seq_len.
+ * Errors: DSA_DECODE_ERR_INVALID (NULL/misaligned pointer, host-only plan,
+ * non-finite scale), DSA_DECODE_ERR_WORKSPACE, DSA_DECODE_ERR_LAUNCH. */
+int dsa_decode_launch(dsa_decode_plan_t plan, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens,
+                      const int32_t* sel_indices, float k_scale, float v_scale,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Copy the normalised selection the last launch on `workspace` computed
+ * (what the attention consumed) into caller device memory, on `stream`:
+ *   ids      int32  [num_rows, sel_width]: row r's distinct valid ids in
+ *            ascending order in its first counts[r] entries; the rest is
+ *            unspecified
+ *   counts   int32  [num_rows]
+ *   offsets  uint64 [num_rows, sel_width]: byte offset of each id's latent
+ *            row in the pool, same order as ids
+ * Any of the three may be NULL. Asynchronous. */
+int dsa_decode_read_selection(dsa_decode_plan_t plan, const void* workspace,
+                              size_t workspace_bytes, int32_t* ids,
+                              int32_t* counts, uint64_t* offsets, void* stream);
+
+/* Per-kernel timing for benchmarks. dsa_decode_timing_begin makes the next
+ * max_launches launches of this plan record HIP events around each kernel
+ * on the launch stream (events are created here, not in the launch).
+ * dsa_decode_timing_end waits for the recorded events and returns, summed
+ * over the recorded launches, the milliseconds spent in the selection,
+ * attend and combine kernels (kernel_ms[0..2]) and the number of launches
+ * recorded; it then stops recording. */
+int dsa_decode_timing_begin(dsa_decode_plan_t plan, int32_t max_launches);
+int dsa_decode_timing_end(dsa_decode_plan_t plan, float* kernel_ms,
+                          int32_t* launches);
+
+/* Thread-local message of the last failure on this thread ("" if none). */
+const char* dsa_decode_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int dsa_decode_version(void);
+
+#define DSA_DECODE_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_DECODE_H */

@@ -1,0 +1,87 @@
+/*
+ * CPU oracle for the selected-index NoPE MLA paged decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may include, link or
+ * call this library: only the tests, the smoke check and the benchmark's CPU
+ * baseline use it. It shares no code, header, table or constant with the HIP
+ * library under sparse_attention_decode_row_amd/csrc.
+ *
+ * Everything is computed in double precision from the definition of the
+ * operation, one row and one head at a time, with no blocking or fusion.
+ *
+ * Sources (the web pages the method is described on):
+ *   [attend]   page "spark_model/layers/glm5next_dsa/attend.rs"
+ *   [decode_k] page "metrale_model_arch/glm5next_dsa/layer/decode_k.rs"
+ *   [build]    page "spark_model/layers/glm5next_dsa/build.rs"
+ *
+ * Parity status: every function here is pinned by CPU tests against
+ * something other than itself (torch's float8 cast, Python set semantics,
+ * a dense masked-attention brute force over a logically contiguous cache,
+ * closed forms). None is "parity unpinned".
+ */
+#ifndef DSA_ORACLE_H
+#define DSA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Value of one OCP FP8 E4M3FN code: 1 sign bit, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 is subnormal (m/8 * 2^-6); the two codes
+ * with all exponent and mantissa bits set are NaN; there is no infinity.
+ * The cache is "FP8" per [attend] DsaDecodeInputs; the E4M3 variant is the
+ * one the decode is specified over. */
+double dsa_oracle_fp8_e4m3fn(uint8_t code);
+
+/* Value of one bfloat16 bit pattern (the upper half of an IEEE binary32). */
+double dsa_oracle_bf16(uint16_t bits);
+
+/* Selection of one row as a set ([attend] module doc, "Why this is not the
+ * masked kernel": membership only, duplicates collapse, -1 is a hole).
+ * Writes the sorted distinct ids t of sel[0..width) with 0 <= t < seq_len to
+ * out_ids (capacity width) and returns their count. Any negative id is a
+ * hole; ids at or beyond seq_len are dropped. */
+int32_t dsa_oracle_select_row(const int32_t* sel, int32_t width,
+                              int32_t seq_len, int32_t* out_ids);
+
+/* Byte offset of logical token t of a row inside the paged pool:
+ * page = bt_row[t / block_size], offset = page * cache_stride_bytes
+ * + (t mod block_size) * kv_lora_rank. One FP8 byte per latent element and a
+ * single KV head ([decode_k] slot computation and DsaDecodePaging stride;
+ * [attend] DsaDecodePaging::validate). */
+uint64_t dsa_oracle_token_offset(const int32_t* bt_row, int32_t t,
+                                 int32_t block_size,
+                                 uint64_t cache_stride_bytes,
+                                 int32_t kv_lora_rank);
+
+/* The whole decode.
+ *   q            [rows, heads, D] bf16 bits (absorbed queries, latent space)
+ *   k_cache      FP8 E4M3FN pool, v_cache the same layout (may alias)
+ *   block_tables [rows, bt_stride] int32; bt_stride 0 = every row uses row 0
+ *   seq_lens     [rows] int32
+ *   sel          [rows, width] int32
+ *   out          [rows, heads, D] double
+ * For each row and head, over the row's selected set S:
+ *   s_t = sm_scale * sum_d q[d] * (k_scale * dec(K_t[d]))
+ *   p_t = exp(s_t - max s), out = sum_t p_t * (v_scale * dec(V_t[d])) / sum p
+ * and out = 0 when S is empty. num_threads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on a bad argument. */
+int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
+                      int32_t width, int32_t block_size, int32_t bt_stride,
+                      uint64_t cache_stride_bytes, double sm_scale,
+                      double k_scale, double v_scale,
+                      const uint16_t* q, const uint8_t* k_cache,
+                      const uint8_t* v_cache, const int32_t* block_tables,
+                      const int32_t* seq_lens, const int32_t* sel,
+                      double* out, int32_t num_threads);
+
+/* Number of threads an OpenMP parallel region of the decode would use. */
+int32_t dsa_oracle_max_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
