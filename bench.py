@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the selected-index NoPE MLA paged decode on one MI355X.
+
+One step = one dsa_decode_launch (selection normalisation + page translation,
+gather-attend, split combine) over one batch of synthetic decode input, with
+every input already resident in HBM. The default workload is the long-context
+decode share: 128 rows x 64 local heads, kv_lora_rank 512, 2048 selected ids
+per row out of a 131072-token context, pages drawn from one 24 GiB FP8 pool.
+Steps cycle through several independently drawn selection batches (and query
+batches) so the gathered rows are not served from the 256 MiB last-level cache
+by the previous step.
+
+Prints one JSON line (rank 0) with the throughput in selected tokens/s, the
+roofline of the attend kernel (gathered FP8 bytes / its HIP-event-timed
+duration against 8 TB/s), the MFMA utilisation, and the CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="long",
+                    choices=["glm", "long", "verify", "ragged"])
+    ap.add_argument("--sets", type=int, default=4,
+                    help="distinct input batches cycled through")
+    ap.add_argument("--cpu-rows", type=int, default=16,
+                    help="rows of the workload the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB "
+                         "(reference dispatch for HBM counter calibration)")
+    ap.add_argument("--chunk-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this decode path is built and measured on one GPU; "
+                          "runs on more than one GPU are not part of it (see DESIGN.md "
+                          "for how it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_decode_row_amd as dsa
+    import workloads as WL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    t0 = time.time()
+
+    base = WL.make(name, with_pool=False)
+    R, H, D, W = base.rows, base.heads, base.D, base.width
+    pool = WL.device_pool(base.num_pages, base.block_size, D, base.sigma,
+                          base.k_scale, seed=base.seed)
+    bt = torch.from_numpy(base.block_tables).to(dev)
+    sl = torch.from_numpy(base.seq_lens).to(dev)
+    batches = []
+    uniq_per_step = []
+    for s in range(args.sets):
+        wl = base if s == 0 else WL.make(name, sel_seed=s, with_pool=False)
+        qb = np.random.default_rng([base.seed, 100 + s]).standard_normal((R, H, D), dtype=np.float32)
+        q = torch.from_numpy(WL.bf16_bits_from_f32(qb).view(np.int16)).to(dev).view(torch.bfloat16)
+        sel = torch.from_numpy(wl.sel).to(dev)
+        batches.append((q, sel))
+        n = 0
+        for r in range(R):
+            row = wl.sel[r]
+            n += int(np.unique(row[(row >= 0) & (row < wl.seq_lens[r])]).size)
+        uniq_per_step.append(n)
+    out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
+    plan = dsa.Plan(num_rows=R, num_q_heads=H, kv_lora_rank=D,
+                    block_size=base.block_size, index_kpool=base.kpool, sel_width=W,
+                    block_table_stride=base.bt_stride, max_seq_len=base.max_seq_len,
+                    sm_scale=base.sm_scale, cache_stride_bytes=base.cache_stride_bytes,
+                    chunk_tokens=args.chunk_tokens, device=0)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    info = plan.info()
+    stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+    print(f"[bench] {name}: rows {R} heads {H} D {D} W {W} pool "
+          f"{base.pool_bytes / 2**30:.1f} GiB, plan {info}, setup {time.time() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    def step(i):
+        q, sel = batches[i % args.sets]
+        plan.launch(q, pool, pool, bt, sl, sel, base.k_scale, base.v_scale, out, ws,
+                    stream=sptr)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        # reference dispatch for counter calibration: reads and writes exactly
+        # calib bytes once each
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+
+    K = args.steps
+    plan.timing_begin(K)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    kernel_ms, launches = plan.timing_end()
+    wall_ms = (t_end - t_start) * 1e3
+    event_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / K
+
+    tokens = float(np.mean([uniq_per_step[(args.warmup + i) % args.sets] for i in range(K)]))
+    value = tokens / (ms_per_step / 1e3)
+    attend_ms = kernel_ms[1] / launches
+    gathered_bytes = tokens * D                      # FP8 latent bytes per launch
+    flops = 4.0 * H * D * tokens                     # QK^T + PV
+    achieved_gbps = gathered_bytes / (attend_ms / 1e3) / 1e9
+    tflops = flops / (attend_ms / 1e3) / 1e12
+
+    result = {
+        "metric": "selected tokens/s per decode step (achieved HBM GB/s & MFMA util of the attend kernel alongside)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{name}: {R} rows x {H} heads, kv_lora_rank {D}, {W} selected ids "
+                        f"per row of a {int(base.max_seq_len)}-token context, block_size "
+                        f"{base.block_size}, FP8 E4M3 pool {base.pool_bytes / 2**30:.1f} GiB",
+            "rows": R, "heads": H, "kv_lora_rank": D, "sel_width": W,
+            "seq_len": int(base.max_seq_len), "block_size": base.block_size,
+            "selected_tokens_per_step": tokens, "input_batches_cycled": args.sets,
+            "plan": info,
+        },
+        "us_per_step": ms_per_step * 1e3,
+        "us_per_step_gpu_events": event_ms * 1e3 / K,
+        "kernel_us": {"select": kernel_ms[0] / launches * 1e3,
+                      "attend": attend_ms * 1e3,
+                      "combine": kernel_ms[2] / launches * 1e3},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "dsa_attend_kernel",
+            "achieved": achieved_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": gathered_bytes,
+        },
+        "mfma": {"achieved": tflops, "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                 "frac": tflops / BF16_DENSE_TFLOPS, "flops_per_launch": flops},
+    }
+
+    if args.cpu_rows > 0:
+        result["cpu_baseline"] = cpu_baseline(base, pool, batches[0], args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, pool_dev, batch, nrows):
+    """The CPU oracle, as it stands, on the first `nrows` rows of the first
+    batch (all heads, the full selection of each row), on this host's cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as WL
+
+    rows = list(range(min(nrows, wl.rows)))
+    pages = WL.pages_of_rows(wl, rows)
+    idx = torch.from_numpy(pages.astype(np.int64)).to(pool_dev.device)
+    sub = pool_dev.view(-1, wl.cache_stride_bytes).index_select(0, idx).cpu().numpy().ravel()
+    remap = np.zeros(wl.num_pages, dtype=np.int32)
+    remap[pages] = np.arange(pages.size, dtype=np.int32)
+    bt = remap[wl.block_tables[rows]]
+    q = batch[0].view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    sel = wl.sel[rows]
+    threads = oracle.max_threads()
+    t = time.perf_counter()
+    oracle.decode(q, sub, None, bt, wl.seq_lens[rows], sel, block_size=wl.block_size,
+                  bt_stride=wl.bt_stride, cache_stride_bytes=wl.cache_stride_bytes,
+                  sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                  num_threads=threads)
+    dt = time.perf_counter() - t
+    tokens = sum(int(np.unique(sel[i][(sel[i] >= 0) & (sel[i] < wl.seq_lens[r])]).size)
+                 for i, r in enumerate(rows))
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.rows} rows of the same workload (all "
+                      f"{wl.heads} heads, {tokens} selected tokens), float64 C oracle, "
+                      f"{dt:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,51 @@
+"""Build libdsa_decode.so in-tree with hipcc for gfx950 only."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libdsa_decode.so")
+SOURCES = [os.path.join(HERE, "csrc", "plan.cpp"),
+           os.path.join(HERE, "csrc", "kernels.hip")]
+HEADERS = [os.path.join(ROOT, "include", "dsa_decode.h"),
+           os.path.join(HERE, "csrc", "plan.hpp")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    return "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-Wall",
+           # packed fp32 arithmetic stays off in device code
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           "-o", LIB + ".tmp"] + SOURCES
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,254 @@
+// Host-side validation and planning of the selected-index NoPE MLA decode.
+//
+// The geometry rules come from the launcher page "spark_model/layers/
+// glm5next_dsa/attend.rs" (DsaDecodePaging::validate and decode_attention's
+// guards) and the block-table capacity check of "metrale_model_arch/
+// glm5next_dsa/layer/decode_k.rs". Every rule is an error with the
+// offending values in the message; nothing falls back to another path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <sstream>
+
+#include "plan.hpp"
+
+namespace dsa {
+
+namespace {
+thread_local std::string g_error;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool supported_rank(int32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+}  // namespace
+
+void set_error(const std::string& msg) { g_error = msg; }
+
+int fail(int status, const std::string& msg) {
+  g_error = msg;
+  return status;
+}
+
+int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
+  if (!p) return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: params is NULL");
+  std::ostringstream m;
+  // A launch with no rows or no heads is refused as degenerate.
+  if (p->num_rows <= 0 || p->num_q_heads <= 0) {
+    m << "dsa_decode_plan: degenerate launch (" << p->num_rows << " rows, "
+      << p->num_q_heads << " heads)";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->block_size <= 0) {
+    m << "dsa_decode_plan: block_size must be > 0, got " << p->block_size;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->index_kpool <= 0) {
+    m << "dsa_decode_plan: index_kpool must be > 0, got " << p->index_kpool;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  // The selector builds pools over absolute positions; a page size that is
+  // not a whole number of pools would split a pool across two pages.
+  if (p->block_size % p->index_kpool != 0) {
+    m << "dsa_decode_plan: block_size " << p->block_size
+      << " is not a multiple of index_kpool " << p->index_kpool
+      << " (a selector pool would straddle a page boundary)";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  // MLA keeps one latent KV head.
+  if (p->num_kv_heads != 1) {
+    m << "dsa_decode_plan: MLA has a single latent KV head, got num_kv_heads "
+      << p->num_kv_heads;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  // The kernels are compiled for a fixed set of latent widths; any other
+  // width would mis-tile silently, so it is refused.
+  if (!supported_rank(p->kv_lora_rank)) {
+    m << "dsa_decode_plan: kv_lora_rank " << p->kv_lora_rank
+      << " is not compiled in (supported: 64, 128, 256, 512)";
+    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
+  }
+  if (p->sel_width <= 0) {
+    m << "dsa_decode_plan: sel_width must be > 0, got " << p->sel_width;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->max_seq_len <= 0) {
+    m << "dsa_decode_plan: max_seq_len must be > 0, got " << p->max_seq_len;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->block_table_stride < 0) {
+    m << "dsa_decode_plan: block_table_stride must be >= 0, got "
+      << p->block_table_stride;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  const uint64_t row_bytes =
+      (uint64_t)p->block_size * (uint64_t)p->kv_lora_rank;
+  const uint64_t stride = p->cache_stride_bytes ? p->cache_stride_bytes : row_bytes;
+  if (stride < row_bytes) {
+    m << "dsa_decode_plan: cache_stride_bytes " << stride
+      << " is smaller than one page (block_size * kv_lora_rank = " << row_bytes << ")";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (stride % 16 != 0) {
+    m << "dsa_decode_plan: cache_stride_bytes " << stride
+      << " is not a multiple of 16";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  // A per-row table must cover every position the row may attend: its entry
+  // count is a number of pages, max_seq_len a number of tokens.
+  if (p->block_table_stride > 0 &&
+      (int64_t)p->max_seq_len > (int64_t)p->block_table_stride * p->block_size) {
+    m << "dsa_decode_plan: max_seq_len " << p->max_seq_len
+      << " tokens needs " << (p->max_seq_len + p->block_size - 1) / p->block_size
+      << " block-table entries per row but block_table_stride is "
+      << p->block_table_stride << " (block_size " << p->block_size << ")";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (!std::isfinite(p->sm_scale)) {
+    m << "dsa_decode_plan: sm_scale must be finite, got " << p->sm_scale;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->chunk_tokens < 0 ||
+      (p->chunk_tokens > 0 && (p->chunk_tokens % kTileTokens != 0 ||
+                               p->chunk_tokens > kMaxChunkTokens))) {
+    m << "dsa_decode_plan: chunk_tokens " << p->chunk_tokens
+      << " must be 0 or a multiple of " << kTileTokens << " up to "
+      << kMaxChunkTokens;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  for (int i = 0; i < 4; ++i)
+    if (p->reserved[i] != 0)
+      return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
+  // Offsets into the selection, q and out are formed in 64-bit arithmetic
+  // on the device; the per-row element counts must fit 32 bits.
+  if ((int64_t)p->num_q_heads * p->kv_lora_rank > INT32_MAX) {
+    m << "dsa_decode_plan: num_q_heads * kv_lora_rank overflows int32";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  *norm = *p;
+  norm->cache_stride_bytes = stride;
+  return DSA_DECODE_OK;
+}
+
+void plan_layout(dsa_decode_plan_s* plan) {
+  const dsa_decode_params& p = plan->p;
+  const int64_t R = p.num_rows, H = p.num_q_heads, D = p.kv_lora_rank,
+                W = p.sel_width;
+  plan->head_blocks = (int)((H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  // A row can attend at most min(W, max_seq_len) distinct tokens.
+  const int64_t wmax = std::min<int64_t>(W, p.max_seq_len);
+  int64_t ct;
+  if (p.chunk_tokens > 0) {
+    ct = p.chunk_tokens;
+  } else {
+    // Spread the largest possible per-row work over the compute units:
+    // tokens one workgroup should take so that rows x head blocks x chunks
+    // is about one workgroup per CU.
+    const int64_t units = R * plan->head_blocks;
+    int64_t per_cu = (wmax * units + plan->num_cus - 1) / plan->num_cus;
+    ct = (per_cu + kTileTokens - 1) / kTileTokens * kTileTokens;
+    ct = std::max<int64_t>(ct, kTileTokens);
+    ct = std::min<int64_t>(ct, kMaxChunkTokens);
+  }
+  const int64_t wmax_tiles = (wmax + kTileTokens - 1) / kTileTokens * kTileTokens;
+  ct = std::min<int64_t>(ct, std::max<int64_t>(wmax_tiles, kTileTokens));
+  plan->chunk_tokens = (int)ct;
+  plan->chunks = (int)((wmax + ct - 1) / ct);
+  if (plan->chunks < 1) plan->chunks = 1;
+
+  WorkspaceLayout& L = plan->ws;
+  size_t off = 0;
+  L.ids = off;
+  off = align_up(off + sizeof(int32_t) * R * W, kWsAlign);
+  L.offsets = off;
+  off = align_up(off + sizeof(uint64_t) * R * W, kWsAlign);
+  L.counts = off;
+  off = align_up(off + sizeof(int32_t) * R, kWsAlign);
+  if (plan->chunks > 1) {
+    L.part_o = off;
+    off = align_up(off + sizeof(float) * R * plan->chunks * H * D, kWsAlign);
+    L.part_ml = off;
+    off = align_up(off + sizeof(float) * R * plan->chunks * H * 2, kWsAlign);
+  }
+  L.total = off;
+}
+
+}  // namespace dsa
+
+extern "C" {
+
+const char* dsa_decode_last_error(void) { return dsa::g_error.c_str(); }
+
+int dsa_decode_version(void) { return DSA_DECODE_VERSION; }
+
+int dsa_decode_plan(const dsa_decode_params* params, int device,
+                    dsa_decode_plan_t* out) {
+  if (!out) return dsa::fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: out is NULL");
+  *out = nullptr;
+  dsa_decode_params norm{};
+  int st = dsa::validate_params(params, &norm);
+  if (st != DSA_DECODE_OK) return st;
+
+  int num_cus = 256;
+  if (device >= 0) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || device >= count) {
+      (void)hipGetLastError();
+      std::ostringstream m;
+      m << "dsa_decode_plan: HIP device " << device << " not found ("
+        << count << " visible)";
+      return dsa::fail(DSA_DECODE_ERR_DEVICE, m.str());
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+      (void)hipGetLastError();
+      return dsa::fail(DSA_DECODE_ERR_DEVICE,
+                       "dsa_decode_plan: hipGetDeviceProperties failed");
+    }
+    // The kernels are gfx950 code objects; any other device is an error,
+    // never a fallback to some other implementation.
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      std::ostringstream m;
+      m << "dsa_decode_plan: device " << device << " is " << prop.gcnArchName
+        << "; this library is built for gfx950 only";
+      return dsa::fail(DSA_DECODE_ERR_DEVICE, m.str());
+    }
+    num_cus = prop.multiProcessorCount;
+  } else if (device != -1) {
+    return dsa::fail(DSA_DECODE_ERR_INVALID,
+                     "dsa_decode_plan: device must be >= 0, or -1 for a host-only plan");
+  }
+
+  dsa_decode_plan_s* plan = new (std::nothrow) dsa_decode_plan_s();
+  if (!plan) return dsa::fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: out of host memory");
+  plan->p = norm;
+  plan->device = device;
+  plan->num_cus = num_cus;
+  dsa::plan_layout(plan);
+  *out = plan;
+  dsa::set_error("");
+  return DSA_DECODE_OK;
+}
+
+size_t dsa_decode_workspace_bytes(dsa_decode_plan_t plan) {
+  return plan ? plan->ws.total : 0;
+}
+
+int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info) {
+  if (!plan || !info)
+    return dsa::fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan_get_info: NULL argument");
+  info->device = plan->device;
+  info->chunk_tokens = plan->chunk_tokens;
+  info->chunks_per_row = plan->chunks;
+  info->head_blocks = plan->head_blocks;
+  info->attend_workgroups = plan->p.num_rows * plan->head_blocks * plan->chunks;
+  info->uses_combine = plan->chunks > 1 ? 1 : 0;
+  info->num_cus = plan->num_cus;
+  info->reserved = 0;
+  info->workspace_bytes = plan->ws.total;
+  return DSA_DECODE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal plan shared by the host planner (plan.cpp) and the launcher
+// (kernels.hip). Not part of the public ABI (include/dsa_decode.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "dsa_decode.h"
+
+namespace dsa {
+
+// Tokens staged in LDS per pipeline step of the attend kernel.
+constexpr int kTileTokens = 64;
+// Largest chunk one attend workgroup handles (its byte-offset table lives in
+// LDS: 2048 x 8 B = 16 KiB).
+constexpr int kMaxChunkTokens = 2048;
+// Heads one attend workgroup covers (4 waves x 16 heads).
+constexpr int kHeadsPerBlock = 64;
+// Workspace sub-buffer alignment.
+constexpr size_t kWsAlign = 256;
+
+struct WorkspaceLayout {
+  size_t ids = 0;       // int32 [R, W]
+  size_t offsets = 0;   // uint64 [R, W]
+  size_t counts = 0;    // int32 [R]
+  size_t part_o = 0;    // float [R, C, H, D]   (C > 1 only)
+  size_t part_ml = 0;   // float [R, C, H, 2]   (C > 1 only)
+  size_t total = 0;
+};
+
+}  // namespace dsa
+
+struct dsa_decode_plan_s {
+  dsa_decode_params p{};          // validated; cache_stride_bytes filled in
+  int device = -1;
+  int num_cus = 256;
+  int chunk_tokens = 0;           // multiple of kTileTokens, <= kMaxChunkTokens
+  int chunks = 1;                 // per row per head block
+  int head_blocks = 1;
+  dsa::WorkspaceLayout ws;
+  // benchmark timing (dsa_decode_timing_begin / _end)
+  std::vector<void*> events;      // hipEvent_t, 4 per recorded launch
+  int timing_capacity = 0;
+  int timing_count = 0;
+};
+
+namespace dsa {
+
+// Thread-local error text.
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+// Pure host validation of params (no GPU needed). Returns a status and sets
+// the error text on failure; fills *norm with the normalised params.
+int validate_params(const dsa_decode_params* p, dsa_decode_params* norm);
+
+// Split decomposition and workspace layout for validated params.
+void plan_layout(dsa_decode_plan_s* plan);
+
+}  // namespace dsa

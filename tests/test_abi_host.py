@@ -1,0 +1,154 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports what
+include/dsa_decode.h declares, the planner's validation rules and the split
+decomposition. Rules cited from the pages:
+  [attend]   "spark_model/layers/glm5next_dsa/attend.rs" (DsaDecodePaging::validate,
+             decode_attention's guards, Glm5NextDsaDecodeKernel::resolve)
+  [decode_k] "metrale_model_arch/glm5next_dsa/layer/decode_k.rs" (block-table
+             capacity check)
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_decode.h")
+
+GOOD = dict(num_rows=128, num_q_heads=64, kv_lora_rank=512, block_size=64,
+            index_kpool=4, sel_width=2048, block_table_stride=2048,
+            max_seq_len=131072, sm_scale=1 / 16)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_decode_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("dsa_decode_plan", "dsa_decode_launch", "dsa_decode_workspace_bytes",
+                 "dsa_decode_plan_destroy", "dsa_decode_last_error"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(native):
+    lib = ctypes.CDLL(native.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in include/dsa_decode.h but not exported"
+    assert set(native.EXPORTED_SYMBOLS) == set(declared_functions())
+
+
+def test_version(native):
+    assert native.lib().dsa_decode_version() == 100
+
+
+def plan(native, **kw):
+    args = dict(GOOD)
+    args.update(kw)
+    return native.Plan(device=-1, **args)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(num_rows=0), -1, "degenerate launch"),
+    (dict(num_q_heads=0), -1, "degenerate launch"),
+    (dict(block_size=0), -1, "block_size must be > 0"),
+    (dict(index_kpool=0), -1, "index_kpool must be > 0"),
+    (dict(block_size=64, index_kpool=6), -1, "not a multiple of index_kpool 6"),
+    (dict(num_kv_heads=2), -1, "single latent KV head"),
+    (dict(kv_lora_rank=576), -2, "not compiled in"),
+    (dict(kv_lora_rank=32), -2, "not compiled in"),
+    (dict(sel_width=0), -1, "sel_width must be > 0"),
+    (dict(max_seq_len=0), -1, "max_seq_len must be > 0"),
+    (dict(block_table_stride=-1), -1, "block_table_stride must be >= 0"),
+    (dict(cache_stride_bytes=1000), -1, "smaller than one page"),
+    (dict(cache_stride_bytes=64 * 512 + 8), -1, "not a multiple of 16"),
+    (dict(block_table_stride=100), -1, "block-table entries per row"),
+    (dict(sm_scale=float("inf")), -1, "sm_scale must be finite"),
+    (dict(chunk_tokens=100), -1, "chunk_tokens"),
+    (dict(chunk_tokens=4096), -1, "chunk_tokens"),
+])
+def test_plan_rejects(native, kw, status, needle):
+    with pytest.raises(native.DsaDecodeError) as e:
+        plan(native, **kw)
+    assert e.value.status == status
+    assert needle in str(e.value)
+    assert needle in native.last_error()
+
+
+def test_plan_rejects_bad_device_argument(native):
+    with pytest.raises(native.DsaDecodeError) as e:
+        native.Plan(device=-5, **GOOD)
+    assert e.value.status == -1
+
+
+def test_no_gpu_means_device_error(native):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(native.DsaDecodeError) as e:
+        native.Plan(device=0, **GOOD)
+    assert e.value.status == native.DSA_DECODE_ERR_DEVICE
+
+
+def test_shared_table_skips_capacity_rule(native):
+    p = plan(native, block_table_stride=0)
+    assert p.workspace_bytes > 0
+
+
+def test_capacity_rule_boundary(native):
+    # exactly enough entries: 2048 * 64 = 131072 positions
+    plan(native, block_table_stride=2048, max_seq_len=131072)
+    with pytest.raises(native.DsaDecodeError):
+        plan(native, block_table_stride=2048, max_seq_len=131073)
+
+
+@pytest.mark.parametrize("kw,chunks,ct", [
+    (dict(), 2, 1024),                                        # 128 rows
+    (dict(num_rows=32, max_seq_len=8192, block_table_stride=128), 8, 256),
+    (dict(num_rows=256, max_seq_len=32768, block_table_stride=512), 1, 2048),
+    (dict(num_rows=2, num_q_heads=4, kv_lora_rank=64, block_size=16,
+          sel_width=32, block_table_stride=16, max_seq_len=173), 1, 64),
+    (dict(chunk_tokens=192), 11, 192),
+    (dict(num_rows=1, sel_width=100, max_seq_len=50, block_table_stride=1), 1, 64),
+])
+def test_split_plan(native, kw, chunks, ct):
+    info = plan(native, **kw).info()
+    assert info["chunks_per_row"] == chunks
+    assert info["chunk_tokens"] == ct
+    assert info["uses_combine"] == (chunks > 1)
+    assert info["device"] == -1
+
+
+def test_workspace_layout(native):
+    p = plan(native)
+    R, W, C, H, D = 128, 2048, 2, 64, 512
+    need = R * W * 4 + R * W * 8 + R * 4 + R * C * H * D * 4 + R * C * H * 2 * 4
+    assert need <= p.workspace_bytes <= need + 5 * 256
+    p1 = plan(native, num_rows=256, max_seq_len=32768, block_table_stride=512)
+    assert p1.info()["chunks_per_row"] == 1
+    assert p1.workspace_bytes <= 256 * 2048 * 12 + 256 * 4 + 3 * 256
+
+
+def test_head_blocks(native):
+    assert plan(native, num_q_heads=64).info()["head_blocks"] == 1
+    assert plan(native, num_q_heads=65).info()["head_blocks"] == 2
+    assert plan(native, num_q_heads=128).info()["head_blocks"] == 2
+
+
+def test_host_only_plan_cannot_launch(native):
+    p = plan(native)
+    with pytest.raises(native.DsaDecodeError) as e:
+        p.launch(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 0.02, 0.02,
+                 1 << 20, 1 << 20, workspace_bytes=p.workspace_bytes, stream=0)
+    assert e.value.status == native.DSA_DECODE_ERR_INVALID
+    assert "host-only" in str(e.value)
+
+
+def test_binding_refuses_without_library(monkeypatch, native):
+    import sparse_attention_decode_row_amd as pkg
+    monkeypatch.setattr(pkg, "_lib", None)
+    monkeypatch.setattr(pkg, "library_path", lambda: "/nonexistent/libdsa_decode.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        pkg.lib()

@@ -1,0 +1,371 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (from the method's contract): per (row, head) the max normwise relative
+error of the BF16 output is <= 1e-2; the set of attended ids and their byte
+offsets are bit-exact. Every case prints its name before it touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+H_ = None
+
+
+@pytest.fixture(scope="module")
+def H(native):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gpu_harness
+    return gpu_harness
+
+
+def _announce(name, **kw):
+    print(f"\n[gpu case] {name} {kw}", flush=True)
+
+
+# ------------------------------------------------------------ workloads
+
+def test_tiny(H):
+    wl = WL.make("tiny")
+    _announce("tiny", rows=wl.rows, heads=wl.heads, D=wl.D)
+    run = H.run_gpu(wl)
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, range(wl.rows))
+    err = H.normwise_err(run.out, want)
+    print(f"tiny max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+def test_glm_full(H):
+    wl = WL.make("glm")
+    _announce("glm", rows=wl.rows, heads=wl.heads, D=wl.D, W=wl.width)
+    run = H.run_gpu(wl)
+    print("plan", run.info)
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, range(wl.rows))
+    err = H.normwise_err(run.out, want)
+    print(f"glm max err {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= H.TOL
+
+
+def test_long_sampled_rows(H):
+    wl = WL.make("long", with_pool=False)
+    _announce("long", rows=wl.rows, heads=wl.heads, pool_gib=wl.pool_bytes / 2**30)
+    pool = WL.device_pool(wl.num_pages, wl.block_size, wl.D, wl.sigma, wl.k_scale,
+                          seed=wl.seed)
+    run = H.run_gpu(wl, k_pool=pool)
+    print("plan", run.info)
+    H.check_selection(wl, run)          # every row, bit-exact
+    rows = [0, 37, 90, 127]
+    sub, view = H.sub_pool_for_rows(wl, pool, rows)
+    del pool
+    torch.cuda.empty_cache()
+    want = H.oracle_rows(view, rows, host_pool=sub)
+    err = H.normwise_err(run.out[rows], want)
+    print(f"long rows {rows} max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+def test_verify_sampled_rows(H):
+    wl = WL.make("verify", with_pool=False)
+    _announce("verify", rows=wl.rows, pages=wl.num_pages)
+    pool = WL.device_pool(wl.num_pages, wl.block_size, wl.D, wl.sigma, wl.k_scale,
+                          seed=wl.seed)
+    run = H.run_gpu(wl, k_pool=pool)
+    print("plan", run.info)
+    H.check_selection(wl, run)
+    rows = [0, 1, 2, 3, 101, 254, 255]
+    sub, view = H.sub_pool_for_rows(wl, pool, rows)
+    want = H.oracle_rows(view, rows, host_pool=sub)
+    err = H.normwise_err(run.out[rows], want)
+    print(f"verify rows {rows} max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+def test_ragged_all_rows(H):
+    wl = WL.make("ragged", with_pool=False)
+    _announce("ragged", rows=wl.rows, heads=wl.heads, pages=wl.num_pages)
+    pool = WL.device_pool(wl.num_pages, wl.block_size, wl.D, wl.sigma, wl.k_scale,
+                          seed=wl.seed)
+    run = H.run_gpu(wl, k_pool=pool)
+    print("plan", run.info)
+    H.check_selection(wl, run)
+    host = pool.cpu().numpy()
+    want = H.oracle_rows(wl, range(wl.rows), host_pool=host)
+    err = H.normwise_err(run.out, want)
+    print(f"ragged max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+# -------------------------------------------------- random shapes and splits
+
+CASES = [
+    # (seed, rows, heads, D, B, max_len, width, chunk_tokens, shared, split_v)
+    (0, 3, 16, 512, 64, 700, 600, 0, False, False),
+    (1, 4, 64, 512, 64, 5000, 1500, 128, False, False),
+    (2, 2, 32, 512, 16, 900, 1000, 64, False, False),
+    (3, 5, 20, 256, 32, 2000, 700, 192, False, False),
+    (4, 3, 80, 128, 16, 400, 300, 0, False, False),
+    (5, 6, 4, 64, 16, 300, 200, 64, True, False),
+    (6, 3, 48, 512, 64, 3000, 2100, 0, False, True),
+    (7, 2, 64, 512, 64, 1000, 900, 256, True, True),
+    (8, 4, 1, 512, 8, 150, 64, 0, False, False),
+    (9, 3, 128, 256, 64, 2600, 2500, 1024, False, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
+def test_random_shapes(H, case):
+    seed, rows, heads, D, B, max_len, width, ct, shared, split_v = case
+    rng = np.random.default_rng(500 + seed)
+    wl = WL.random_case(rng, rows=rows, heads=heads, D=D, block_size=B,
+                        max_len=max_len, width=width, shared_table=shared)
+    _announce("random", seed=seed, rows=rows, heads=heads, D=D, W=width,
+              chunk=ct, shared=shared, split_v=split_v)
+    v_host = None
+    v_dev = None
+    if split_v:
+        v_host = WL.host_pool(rng, wl.num_pages, B, D, 1.0, wl.k_scale)
+        v_dev = H.u8(v_host)
+    run = H.run_gpu(wl, v_pool=v_dev, chunk_tokens=ct)
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, range(rows), host_v_pool=v_host)
+    err = H.normwise_err(run.out, want)
+    print(f"case {seed}: plan {run.info} max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+def test_split_invariance(H):
+    rng = np.random.default_rng(42)
+    wl = WL.random_case(rng, rows=3, heads=64, D=512, block_size=64,
+                        max_len=6000, width=2048, hole_frac=0.0, dup_frac=0.0,
+                        oob_frac=0.0)
+    outs = []
+    for ct in (0, 64, 192, 512, 2048):
+        _announce("split", chunk=ct)
+        run = H.run_gpu(wl, chunk_tokens=ct, with_selection=False)
+        outs.append(run.out)
+    want = H.oracle_rows(wl, range(3))
+    for o in outs:
+        assert H.normwise_err(o, want).max() <= H.TOL
+        assert H.normwise_err(o, outs[0]).max() <= H.TOL
+
+
+# ------------------------------------------------------------ special cases
+
+def test_single_token_is_exact_dequantised_row(H):
+    """One selected token (repeated, among holes): the output of every head
+    is bf16(v_scale * dec(code)) bit for bit. The latent row holds all 254
+    finite codes, so this also checks the FP8 decode exhaustively."""
+    D, B = 512, 64
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    row = np.resize(codes, D)   # 254 codes, repeated to fill the row
+    pool = np.zeros(4 * B * D, np.uint8)
+    rng = np.random.default_rng(9)
+    bt = np.array([[3, 1], [2, 0]], np.int32)
+    seq_lens = np.array([100, 128], np.int32)
+    sel = np.full((2, 16), -1, np.int32)
+    t = [77, 5]
+    for r in range(2):
+        page = bt[r, t[r] // B]
+        base = (page * B + t[r] % B) * D
+        pool[base:base + D] = row
+        sel[r, ::4] = t[r]
+    for vs in (1.0, 0.02):
+        wl = WL.Workload(name="single", rows=2, heads=16, D=D, block_size=B, kpool=4,
+                         width=16, bt_stride=2, cache_stride_bytes=B * D,
+                         max_seq_len=128, num_pages=4, sm_scale=1 / 16, k_scale=0.02,
+                         v_scale=vs, sigma=1.0, seed=0,
+                         q_bits=WL.bf16_bits_from_f32(rng.standard_normal((2, 16, D), dtype=np.float32)),
+                         block_tables=bt, seq_lens=seq_lens, sel=sel, pool=pool)
+        _announce("single token", v_scale=vs)
+        run = H.run_gpu(wl)
+        dec = torch.from_numpy(row.copy()).view(torch.float8_e4m3fn).float()
+        # the output is a weighted sum that starts from +0, so the -0 code
+        # comes out as +0 (IEEE: +0 + -0 = +0); the oracle does the same
+        want = (dec * torch.tensor(vs, dtype=torch.float32) + 0.0).to(torch.bfloat16)
+        want_bits = want.view(torch.int16).numpy().view(np.uint16)
+        for r in range(2):
+            for h in range(16):
+                assert np.array_equal(run.out_bits[r, h], want_bits), (vs, r, h)
+
+
+def test_empty_selection_rows_are_zero(H):
+    rng = np.random.default_rng(10)
+    wl = WL.random_case(rng, rows=4, heads=64, D=512, block_size=64, max_len=500,
+                        width=300)
+    sel = wl.sel.copy()
+    seq_lens = wl.seq_lens.copy()
+    sel[0] = -1                              # all holes
+    sel[1] = seq_lens[1] + np.arange(300)    # all past the end
+    seq_lens[2] = 0                          # nothing valid
+    for ct in (0, 64):
+        _announce("empty rows", chunk=ct)
+        run = H.run_gpu(wl, sel=sel, seq_lens=seq_lens, chunk_tokens=ct)
+        H.check_selection(wl, run, sel=sel, seq_lens=seq_lens)
+        assert np.array_equal(run.out_bits[:3], np.zeros_like(run.out_bits[:3]))
+        want = H.oracle_rows(wl, [3], sel=sel, seq_lens=seq_lens)
+        assert H.normwise_err(run.out[3:4], want).max() <= H.TOL
+
+
+def test_repeats_holes_and_order_do_not_change_the_result(H):
+    """The selection is normalised to a sorted set before the attention, so
+    the output is bit-identical whatever the repeats, holes and order."""
+    rng = np.random.default_rng(11)
+    wl = WL.random_case(rng, rows=3, heads=64, D=512, block_size=64, max_len=3000,
+                        width=700, hole_frac=0.0, dup_frac=0.0, oob_frac=0.0)
+    _announce("invariance clean")
+    base = H.run_gpu(wl, with_selection=False)
+    W2 = 1400
+    sel2 = np.full((3, W2), -1, np.int32)
+    for r in range(3):
+        row = np.concatenate([wl.sel[r], wl.sel[r][: 400], np.full(250, -1),
+                              wl.seq_lens[r] + np.arange(50)]).astype(np.int32)
+        rng.shuffle(row)
+        sel2[r] = row
+    wl2 = WL.Workload(**{**wl.__dict__, "width": W2, "sel": sel2})
+    _announce("invariance noisy")
+    noisy = H.run_gpu(wl2)
+    H.check_selection(wl2, noisy)
+    assert np.array_equal(noisy.out_bits, base.out_bits)
+
+
+def test_uniform_softmax_membership_probe(H):
+    """q = 0 makes every selected token weigh 1/n. With one-hot V rows
+    (token t's latent row is e_t with FP8 1.0, v_scale 1) the output is
+    nonzero exactly on the selected set, every nonzero equal to bf16(1/n):
+    a duplicate counted twice or a stray token would show."""
+    D, B, L = 512, 64, 500
+    rng = np.random.default_rng(12)
+    pages = -(-L // B)
+    bt = rng.permutation(pages).astype(np.int32)[None, :]
+    pool = np.zeros(pages * B * D, np.uint8)
+    for t in range(L):
+        base = (bt[0, t // B] * B + t % B) * D
+        pool[base + t] = 0x38   # 1.0
+    sel = rng.integers(-3, L + 30, size=(1, 900)).astype(np.int32)
+    wl = WL.Workload(name="probe", rows=1, heads=16, D=D, block_size=B, kpool=4,
+                     width=900, bt_stride=pages, cache_stride_bytes=B * D,
+                     max_seq_len=L, num_pages=pages, sm_scale=1.0, k_scale=1.0,
+                     v_scale=1.0, sigma=1.0, seed=0,
+                     q_bits=np.zeros((1, 16, D), np.uint16), block_tables=bt,
+                     seq_lens=np.array([L], np.int32), sel=sel, pool=pool)
+    for ct in (0, 64):
+        _announce("membership probe", chunk=ct)
+        run = H.run_gpu(wl, chunk_tokens=ct)
+        S = sorted({int(t) for t in sel[0] if 0 <= t < L})
+        inv_n = torch.tensor(1.0 / len(S), dtype=torch.float32).to(torch.bfloat16).float().item()
+        for h in range(16):
+            nz = np.flatnonzero(run.out[0, h])
+            assert nz.tolist() == S
+            np.testing.assert_allclose(run.out[0, h, S], inv_n, rtol=2 ** -7)
+
+
+def test_two_window_selection_beyond_262144_positions(H):
+    """Rows longer than one selection-bitmap window (262144 positions)."""
+    rng = np.random.default_rng(13)
+    D, B, L = 512, 64, 600_000
+    n_pages = 96
+    per_row = -(-L // B)
+    bt = rng.integers(0, n_pages, size=(2, per_row)).astype(np.int32)
+    sel = rng.integers(-10, L + 100, size=(2, 3000)).astype(np.int32)
+    sel[:, :500] = rng.integers(262_000, 262_300, size=(2, 500))   # around the window edge
+    pool = WL.host_pool(rng, n_pages, B, D, 1.0, 0.02)
+    wl = WL.Workload(name="window", rows=2, heads=64, D=D, block_size=B, kpool=4,
+                     width=3000, bt_stride=per_row, cache_stride_bytes=B * D,
+                     max_seq_len=L, num_pages=n_pages, sm_scale=1 / 16, k_scale=0.02,
+                     v_scale=0.02, sigma=1.0, seed=0,
+                     q_bits=WL.bf16_bits_from_f32(rng.standard_normal((2, 64, D), dtype=np.float32)),
+                     block_tables=bt, seq_lens=np.array([L, 400_000], np.int32), sel=sel,
+                     pool=pool)
+    _announce("two windows", L=L)
+    run = H.run_gpu(wl)
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, [0, 1])
+    assert H.normwise_err(run.out, want).max() <= H.TOL
+
+
+def test_padded_page_stride(H):
+    rng = np.random.default_rng(14)
+    wl = WL.random_case(rng, rows=3, heads=64, D=512, block_size=16, max_len=800,
+                        width=500)
+    # re-lay the pool with a 4 KiB gap after every page
+    stride = wl.block_size * wl.D + 4096
+    pages = wl.pool.reshape(wl.num_pages, -1)
+    big = np.full((wl.num_pages, stride), 0x7F, np.uint8)   # gaps hold NaN codes
+    big[:, : pages.shape[1]] = pages
+    wl2 = WL.Workload(**{**wl.__dict__, "cache_stride_bytes": stride,
+                         "pool": big.ravel()})
+    _announce("padded stride", stride=stride)
+    run = H.run_gpu(wl2)
+    H.check_selection(wl2, run)
+    want = H.oracle_rows(wl2, range(3))
+    assert H.normwise_err(run.out, want).max() <= H.TOL
+
+
+def test_deterministic(H):
+    wl = WL.make("glm")
+    _announce("determinism")
+    pool = H.u8(wl.pool)
+    a = H.run_gpu(wl, k_pool=pool, with_selection=False)
+    b = H.run_gpu(wl, k_pool=pool, with_selection=False)
+    assert np.array_equal(a.out_bits, b.out_bits)
+
+
+# ------------------------------------------------------------ launch errors
+
+def test_launch_rejects_bad_arguments(H):
+    import sparse_attention_decode_row_amd as dsa
+    wl = WL.make("tiny")
+    _announce("launch errors")
+    plan = H.plan_for(wl)
+    q = H.q_tensor(wl.q_bits)
+    pool = H.u8(wl.pool)
+    bt, sl, sel = H.i32(wl.block_tables), H.i32(wl.seq_lens), H.i32(wl.sel)
+    out = torch.empty_like(q)
+    ws = torch.empty(plan.workspace_bytes + 512, dtype=torch.uint8, device=q.device)
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws,
+                    workspace_bytes=plan.workspace_bytes - 1)
+    assert e.value.status == dsa.DSA_DECODE_ERR_WORKSPACE
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws.data_ptr() + 8,
+                    workspace_bytes=plan.workspace_bytes)
+    assert e.value.status == dsa.DSA_DECODE_ERR_WORKSPACE
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.launch(q.data_ptr() + 2, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws)
+    assert e.value.status == dsa.DSA_DECODE_ERR_INVALID
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.launch(q, pool, pool, bt, sl, 0, 0.05, 0.05, out, ws)
+    assert e.value.status == dsa.DSA_DECODE_ERR_INVALID
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.launch(q, pool, pool, bt, sl, sel, float("nan"), 0.05, out, ws)
+    assert e.value.status == dsa.DSA_DECODE_ERR_INVALID
+    host_plan = dsa.Plan(num_rows=2, num_q_heads=4, kv_lora_rank=64, block_size=16,
+                         index_kpool=4, sel_width=32, block_table_stride=16,
+                         max_seq_len=173, sm_scale=0.125, device=-1)
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        host_plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws)
+    assert e.value.status == dsa.DSA_DECODE_ERR_INVALID
+    # nothing was launched: out is untouched by the refused calls
+    plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws)
+    torch.cuda.synchronize()
+
+
+def test_plan_on_gfx950_device(H):
+    import sparse_attention_decode_row_amd as dsa
+    _announce("device plan")
+    p = dsa.Plan(num_rows=128, num_q_heads=64, kv_lora_rank=512, block_size=64,
+                 index_kpool=4, sel_width=2048, block_table_stride=2048,
+                 max_seq_len=131072, sm_scale=1 / 16, device=0)
+    info = p.info()
+    assert info["device"] == 0 and info["num_cus"] >= 1
+    props = torch.cuda.get_device_properties(0)
+    assert props.gcnArchName.startswith("gfx950")
