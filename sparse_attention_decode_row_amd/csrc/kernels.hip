@@ -15,15 +15,22 @@
 //                       byte offset of its FP8 latent row through the block
 //                       table ([decode_k] slot of a position).
 //   dsa_attend_kernel   one workgroup per (row, 64-head block, chunk of the
-//                       sorted set). 64-token tiles of latent rows are DMA'd
-//                       straight into LDS, three deep. Each wave owns 16
-//                       heads: S^T = K Q^T and O^T = V^T P^T run on bf16
-//                       MFMA (16x16x32) with the FP8 rows converted to bf16
-//                       on the LDS->register path; the V operand comes from
-//                       ds_read_tr8_b64, which hands each lane 8 tokens of
-//                       one latent column. Online softmax in the exp2 domain.
-//                       One chunk: the BF16 output is written directly;
-//                       several: fp32 partials plus (max, sum) per head.
+//                       sorted set); 128-token tiles of latent rows are DMA'd
+//                       straight into LDS, double buffered. Each wave owns 16
+//                       heads. Both contractions run on the FP8 matrix cores
+//                       (16x16x128, fp32 accumulation) with the cached latent
+//                       bytes as they are, so nothing is converted per token:
+//                         S^T = K Q^T : Q (bf16) enters as an exact sum of two
+//                                       FP8 terms under a per-head power-of-two
+//                                       scale (8 significant bits = 4 + 4);
+//                         O^T = V^T P^T: the softmax weights enter as a sum of
+//                                       two FP8 terms (relative error <= 2^-9,
+//                                       below bf16's 2^-8); the V operand comes
+//                                       from ds_read_tr8_b64, which hands each
+//                                       lane 8 tokens of one latent column.
+//                       Online softmax in the exp2 domain. One chunk per row:
+//                       the BF16 output is written directly; several: fp32
+//                       partials plus (max, sum) per head.
 //   dsa_combine_kernel  merges the chunk partials of a row
 //                       (log-sum-exp weights) and writes BF16.
 #include <hip/hip_runtime.h>
@@ -31,6 +38,7 @@
 #include <cmath>
 #include <cstdint>
 #include <sstream>
+#include <type_traits>
 
 #include "plan.hpp"
 
@@ -39,9 +47,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define DSA_LDS __attribute__((address_space(3)))
 
@@ -64,31 +73,46 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 8 FP8 E4M3FN codes (two dwords, little-endian byte order) -> 8 bf16.
-// The conversion is exact: every finite E4M3FN value is a bf16 value.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(unsigned lo, unsigned hi) {
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  return r;
+// D = 16x16 fp32 += A (16x128 FP8 E4M3) * B (128x16 FP8 E4M3). Lane l holds
+// A row l%16 and B column l%16, k = 32*(l/16) + [0, 32) as 32 bytes.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// Four floats -> four FP8 E4M3 codes (round to nearest even), byte i = x_i.
+__device__ __forceinline__ int pack_fp8x4(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+}
+
+// x = hi + lo with hi, lo FP8: hi is x rounded to 4 significant bits and lo
+// the exactly computed remainder rounded to 4 more. For |x| < 448 the
+// remainder is a multiple of x's last bf16 bit and at most 8 of them, so a
+// bf16 x (8 significant bits) is represented exactly while lo stays in the
+// FP8 normal/subnormal range; otherwise the error is at most half of lo's
+// last place (relative 2^-9).
+__device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float x3,
+                                            int& hi, int& lo) {
+  hi = pack_fp8x4(x0, x1, x2, x3);
+  const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+  const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  lo = pack_fp8x4(x0 - h01[0], x1 - h01[1], x2 - h23[0], x3 - h23[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
 // LDS layout of one staged tile: token-major rows of D bytes; the 16-byte
 // chunks of a row are XOR-permuted by the token index so that the 16 tokens
-// an MFMA reads at one logical column land in distinct bank groups.
+// one MFMA operand read touches, and the 8 rows of one transposing read,
+// land in distinct bank groups.
 template <int D>
 __device__ __forceinline__ int tile_swizzle(int tok) {
   constexpr int kChunks = D / 16;
   constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
-  return tok & kMask;
+  return ((tok & 15) ^ ((tok & 16) >> 1)) & kMask;
 }
 template <int D>
 __device__ __forceinline__ int tile_offset(int tok, int chunk) {
@@ -98,7 +122,8 @@ __device__ __forceinline__ int tile_offset(int tok, int chunk) {
 // ---------------------------------------------------- selection normalisation
 
 constexpr int kSelThreads = 256;
-constexpr int kWindowWords = 8192;  // 262144 positions per pass over the row
+constexpr int kWindowWords = 8192;   // 262144 positions per pass over the row
+constexpr int kSelIdsLds = 4096;     // sorted ids kept in LDS when W fits
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -139,6 +164,7 @@ struct SelectArgs {
 
 __global__ __launch_bounds__(kSelThreads) void dsa_select_kernel(SelectArgs a) {
   __shared__ uint32_t bitmap[kWindowWords];
+  __shared__ int32_t ids_lds[kSelIdsLds];
   __shared__ int scan_sh[kSelThreads / kWave];
   const int r = blockIdx.x, tid = threadIdx.x;
   int L = a.seq_lens[r];
@@ -147,13 +173,16 @@ __global__ __launch_bounds__(kSelThreads) void dsa_select_kernel(SelectArgs a) {
   const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
   int32_t* idrow = a.ids + (size_t)r * a.width;
   uint64_t* offrow = a.offsets + (size_t)r * a.width;
+  const bool ids_in_lds = a.width <= kSelIdsLds;
+
+  // Phase 1: membership bitmap per window of positions, read back in order.
   int total = 0;
   for (int base = 0; base < L; base += kWindowWords * 32) {
     const int span = min(kWindowWords * 32, L - base);
     const int nwords = (span + 31) >> 5;
     for (int i = tid; i < nwords; i += kSelThreads) bitmap[i] = 0u;
     __syncthreads();
-    // membership: a hole (any negative id) or an id outside [0, L) sets nothing
+    // a hole (any negative id) or an id outside [0, L) sets nothing
     for (int j = tid; j < a.width; j += kSelThreads) {
       const int t = srow[j];
       if (t >= base && t - base < span)
@@ -172,15 +201,37 @@ __global__ __launch_bounds__(kSelThreads) void dsa_select_kernel(SelectArgs a) {
         const int b = __ffs(bits) - 1;
         bits &= bits - 1;
         const int t = base + (w << 5) + b;
-        idrow[pos] = t;
-        const uint32_t page = (uint32_t)bt[t / a.block_size];
-        offrow[pos] = (uint64_t)page * a.cache_stride +
-                      (uint64_t)(t % a.block_size) * (uint64_t)a.D;
+        if (ids_in_lds) ids_lds[pos] = t;
+        else idrow[pos] = t;
         ++pos;
       }
     }
     total += blk_total;
     __syncthreads();
+  }
+
+  // Phase 2: ids in order -> byte offsets, four independent table lookups
+  // in flight per thread.
+  for (int i0 = tid; i0 < total; i0 += 4 * kSelThreads) {
+    int t[4];
+    uint32_t page[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kSelThreads;
+      t[u] = i < total ? (ids_in_lds ? ids_lds[i] : idrow[i]) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      page[u] = i0 + u * kSelThreads < total ? (uint32_t)bt[t[u] / a.block_size] : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kSelThreads;
+      if (i < total) {
+        if (ids_in_lds) idrow[i] = t[u];
+        offrow[i] = (uint64_t)page[u] * a.cache_stride +
+                    (uint64_t)(t[u] % a.block_size) * (uint64_t)a.D;
+      }
+    }
   }
   if (tid == 0) a.counts[r] = total;
 }
@@ -205,26 +256,72 @@ struct AttendArgs {
   float v_scale;
 };
 
+// Value of the lane 16 (resp. 32) apart, and max-reductions over those lane
+// pairs, through the cross-row lane swaps (no LDS traffic).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int partner_xor32(int x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return (int)((lane & 32) ? r[0] : r[1]);
+}
+
+// O^T (16 latent columns x 16 heads) += V^T P^T over 128 tokens, with P given
+// as FP8 codes under per-block E8M0 exponents (scale_b) and V unscaled.
+__device__ __forceinline__ f32x4 mfma_fp8_pscaled(i32x8 v, i32x8 p, int pscale, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v, p, c, 0, 0, 0, 127, 0, pscale);
+}
+
+// How far (log2 domain) a score may exceed the per-head reference before the
+// chunk is recomputed against the exact maximum: weights up to 2^96 keep the
+// E8M0 block exponents in range and the fp32 sums (at most 2^96 * 448 * 2048
+// per element) finite.
+constexpr float kSlack = 96.0f;
+
 // kTS: waves that share one 16-head group and split each tile's tokens
 // (1 when the block has 64 heads, 2 for 32, 4 for 16 or fewer).
-template <int D, int kTS, bool kSplitV, int kStages>
+// kSplitV: V is read from its own buffer (staged next to K).
+template <int D, int kTS, bool kSplitV>
 __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
-  constexpr int kSteps = D / 32;          // QK MFMA steps over the latent width
-  constexpr int kReads = D / 64;          // 16-byte LDS reads per lane per token
-  constexpr int kDBlocks = D / 16;        // PV output column blocks
-  constexpr int kTileBytes = kTileTokens * D;
+  constexpr int kTile = kSplitV ? 64 : 128;         // tokens per stage
+  constexpr int kStages = 2;
+  constexpr int kKSteps = (D + 127) / 128;         // QK MFMA steps over the latent width
+  constexpr int kDBlocks = D / 16;                 // PV output column blocks
+  constexpr int kChunks = D / 16;                  // 16-byte chunks per latent row
+  constexpr int kChunkMask = (kChunks < 16 ? kChunks : 16) - 1;
+  constexpr int kJ0 = kDBlocks < 16 ? kDBlocks : 16;
+  constexpr int kJ1 = kDBlocks / kJ0;              // 2 when D = 512
+  constexpr int kTileBytes = kTile * D;
   constexpr int kStageBytes = kTileBytes * (kSplitV ? 2 : 1);
   constexpr int kLanesPerTok = D / 16;
   constexpr int kTokPerInstr = kWave / kLanesPerTok;
   constexpr int kInstrPerWave = kTileBytes / (kWave * 16) / kWaves;
-  constexpr int kLoadsPerTile = kInstrPerWave * (kSplitV ? 2 : 1);
-  constexpr int kGroups = kWaves / kTS;   // 16-head groups per workgroup
-  constexpr int kNB = 4 / kTS;            // 16-token blocks per wave per tile
+  constexpr int kGroups = kWaves / kTS;            // 16-head groups per workgroup
+  constexpr int kNB = kTile / 16 / kTS;            // 16-token blocks per wave per tile (<= 8)
   constexpr int kSlotFloats = kDBlocks * 4 * kWave + 2 * kWave;
   static_assert(kInstrPerWave >= 1, "tile too small for the DMA split");
-  static_assert(kStages >= 2 && kStages <= 4, "pipeline depth");
+  static_assert(kNB >= 1 && kNB <= 8, "one PV operand covers 8 blocks of 16 tokens");
   static_assert(kTS == 1 || 2 * kSlotFloats * 4 <= kStages * kStageBytes,
                 "merge scratch must fit in the tile buffers");
+  static_assert(16 * 7 * D + 256 * ((kKSteps - 1) >> 1) < 65536,
+                "K operand offsets must fit the LDS instruction offset field");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
   __shared__ uint64_t offs_lds[kMaxChunkTokens];
@@ -245,27 +342,54 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
   const int n_row = a.counts[r];
   const int cstart = c * a.chunk_tokens;
   const int n = max(0, min(a.chunk_tokens, n_row - cstart));
-  const int ntiles = (n + kTileTokens - 1) / kTileTokens;
+  const int ntiles = (n + kTile - 1) / kTile;
 
   // Byte offsets of this chunk's rows, padded to whole tiles with the last
   // real row (the padding is loaded but weighted by exactly zero).
   const uint64_t* orow = a.offsets + (size_t)r * a.width + cstart;
-  for (int i = tid; i < ntiles * kTileTokens; i += kThreads)
-    offs_lds[i] = orow[min(i, n - 1)];
+  for (int i = tid; i < ntiles * kTile; i += kThreads) offs_lds[i] = orow[min(i, n - 1)];
 
-  // This lane's query slice, the B operand of S^T = K Q^T: step j = 2*rr + hh
-  // covers latent columns 64*rr + 16*g + 8*hh + [0, 8).
-  bf16x8 qv[kSteps];
+  // ---- query slice of this lane: head li, latent columns 128*ks + 32*g + [0, 32)
+  // as two FP8 terms under a per-head power-of-two scale that puts the head's
+  // largest |q| in [128, 256).
+  i32x8 qhi[kKSteps], qlo[kKSteps];
+  float score_scale;
   {
+    u32x4 raw[kKSteps][4];
+    float amax = 0.f;
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (head_ok ? head : 0)) * D;
 #pragma unroll
-    for (int rr = 0; rr < kReads; ++rr)
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const int d0 = 128 * ks + 32 * g;
+      const bool ok = head_ok && d0 < D;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (head_ok) v = *(const u32x4*)(qrow + 64 * rr + 16 * g + 8 * hh);
-        qv[2 * rr + hh] = __builtin_bit_cast(bf16x8, v);
+      for (int v = 0; v < 4; ++v) {
+        raw[ks][v] = ok ? *(const u32x4*)(qrow + d0 + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[ks][v][e])), fabsf(bf16_hi(raw[ks][v][e]))));
       }
+    }
+    amax = max_xor32(max_xor16(amax));
+    int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
+    int sh = 7 - e;
+    sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+    const float qs = __uint_as_float((uint32_t)(127 + sh) << 23);       // 2^sh
+    const float qs_inv = __uint_as_float((uint32_t)(127 - sh) << 23);   // 2^-sh
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const unsigned w0 = raw[ks][v][2 * h2], w1 = raw[ks][v][2 * h2 + 1];
+          int hi, lo;
+          split_fp8x4(bf16_lo(w0) * qs, bf16_hi(w0) * qs, bf16_lo(w1) * qs, bf16_hi(w1) * qs,
+                      hi, lo);
+          qhi[ks][2 * v + h2] = hi;
+          qlo[ks][2 * v + h2] = lo;
+        }
+    score_scale = a.scale_log2 * qs_inv;
   }
   __syncthreads();
 
@@ -276,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
       const int gi = wave * kInstrPerWave + k;
       const int tt = gi * kTokPerInstr + lane / kLanesPerTok;
       const int ci = lane % kLanesPerTok;
-      const uint64_t off = offs_lds[tile * kTileTokens + tt] +
+      const uint64_t off = offs_lds[tile * kTile + tt] +
                            (uint64_t)((ci ^ tile_swizzle<D>(tt)) << 4);
       __builtin_amdgcn_global_load_lds(a.k_cache + off,
                                        (DSA_LDS void*)(sbase + gi * (kWave * 16)),
@@ -288,103 +412,195 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
     }
   };
 
+  // K operand addresses. Token 16*b + li, chunk 8*ks + 2*g + h sits at chunk
+  // position (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position is
+  // 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ b) & 1)), so four per-lane
+  // offsets plus compile-time immediates cover every read.
+  int kofs[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      kofs[p][h] = li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
+
+  // V operand rows: read q (0..3) of a PV operand covers operand bytes
+  // 8q..8q+7, i.e. block slots 2q and 2q+1; lanes 2k and 2k+1 of a 16-lane
+  // group supply row k (halves 0 and 1).
+  int vrow[4], vswz[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rrow = li >> 1;
+    const int slot = 2 * q + (rrow >> 2);
+    const int b = slot < kNB ? tp + kTS * slot : tp;   // slots past this wave's blocks weigh zero
+    const int tok = 16 * b + 4 * g + (rrow & 3);
+    vrow[q] = tok * D + 8 * (li & 1);
+    vswz[q] = tile_swizzle<D>(tok) << 4;
+  }
+
+  // The accumulators are touched only by the matrix cores inside the tile
+  // loop: softmax weights are taken against a fixed per-head reference (the
+  // first tile's max). Each 16-token x 2-lane-group block of weights carries
+  // its own E8M0 exponent, so a later score may exceed the reference by up
+  // to 2^kSlack without leaving the FP8 range or fp32 accumulation. Should a
+  // score ever exceed it by more (only with pathological inputs), the chunk
+  // is recomputed with the reference set to the exact maximum seen.
+  DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
+  __shared__ int redo_flag;
   f32x4 O[kDBlocks];
+  float l_part = 0.f;       // this lane's share of sum_t 2^(s_t - m_ref)
+  float m_ref = -INFINITY;  // reference of this head's scores (log2 domain)
+  float m_seen = -INFINITY; // exact max of this head's scores so far
+
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int jd = 0; jd < kDBlocks; ++jd) O[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of this head's scores (log2 domain)
-  float l_part = 0.f;       // this lane's share of the running sum
+    for (int jd = 0; jd < kDBlocks; ++jd) O[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_part = 0.f;
+    if (pass == 1) m_ref = m_seen;
+    bool overflow = false;
+    if (tid == 0) redo_flag = 0;
 
-  for (int s = 0; s < kStages - 1 && s < ntiles; ++s) issue_tile(s, s);
+    if (ntiles > 0) issue_tile(0, 0);
+    for (int it = 0; it < ntiles; ++it) {
+      wait_vmcnt<0>();
+      barrier_lds();  // tile `it` is in LDS for every wave; tile it-1 is consumed
+      if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) % kStages);
 
-  for (int it = 0; it < ntiles; ++it) {
-    // Tiles issued after this one: min(kStages - 2, ntiles - 1 - it).
-    const int ahead = min(kStages - 2, ntiles - 1 - it);
-    if (ahead >= 2) wait_vmcnt<2 * kLoadsPerTile>();
-    else if (ahead == 1) wait_vmcnt<kLoadsPerTile>();
-    else wait_vmcnt<0>();
-    barrier_lds();  // every wave's rows of tile `it` are in LDS; tile it-1 is consumed
-    if (it + kStages - 1 < ntiles) issue_tile(it + kStages - 1, (it + kStages - 1) % kStages);
+      const int stage_off = (it % kStages) * kStageBytes;
+      const DSA_LDS uint8_t* kt = lds + stage_off;
+      const DSA_LDS uint8_t* vt = kSplitV ? kt + kTileBytes : kt;
 
-    const uint8_t* kt = smem + (it % kStages) * kStageBytes;
-    const uint8_t* vt = kSplitV ? kt + kTileBytes : kt;
-
-    // ---- S^T = K Q^T for this wave's 16-token blocks
-    f32x4 S[kNB];
+      // ---- S^T = K Q^T, K operands prefetched two MFMA steps ahead
+      constexpr int kSteps = kNB * kKSteps;
+      auto load_k = [&](int s) -> i32x8 {
+        const int k = s / kKSteps, ks = s % kKSteps;
+        const int b = tp + kTS * k;
+        i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (128 * ks + 32 * g < D) {
+          const int p = (ks ^ b) & 1;
+          const DSA_LDS uint8_t* base = kt + 16 * b * D + 256 * (ks >> 1);
+          const u32x4 lo = *(const DSA_LDS u32x4*)(base + kofs[p][0]);
+          const u32x4 hi = *(const DSA_LDS u32x4*)(base + kofs[p][1]);
+          kop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        return kop;
+      };
+      f32x4 S[kNB];
+      i32x8 kbuf[3];
+      kbuf[0] = load_k(0);
+      if (kSteps > 1) kbuf[1] = load_k(1);
 #pragma unroll
-    for (int k = 0; k < kNB; ++k) {
-      const int tok = 16 * (tp + kTS * k) + li;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int rr = 0; rr < kReads; ++rr) {
-        const u32x4 kv = *(const u32x4*)(kt + tile_offset<D>(tok, 4 * rr + g));
-        acc = mfma16(fp8x8_to_bf16x8(kv.x, kv.y), qv[2 * rr], acc);
-        acc = mfma16(fp8x8_to_bf16x8(kv.z, kv.w), qv[2 * rr + 1], acc);
+      for (int s = 0; s < kSteps; ++s) {
+        const int k = s / kKSteps, ks = s % kKSteps;
+        if (s + 2 < kSteps) kbuf[(s + 2) % 3] = load_k(s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        S[k] = mfma_fp8(kbuf[s % 3], qhi[ks], S[k]);
+        S[k] = mfma_fp8(kbuf[s % 3], qlo[ks], S[k]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      S[k] = acc;
+
+      // ---- weights; lane holds head li, tokens 16*b + 4*g + i. Slots 0-3 and
+      // 4-7 of the lane, each joined with the lane 16 apart, are the blocks
+      // that share one FP8 exponent.
+      const int nvalid = n - it * kTile;
+      if (__builtin_expect(nvalid < kTile, 0)) {
+#pragma unroll
+        for (int k = 0; k < kNB; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * (tp + kTS * k) + 4 * g + i >= nvalid) S[k][i] = -INFINITY;
+      }
+      float mlo = -INFINITY, mhi = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        const float m4 = fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3]));
+        if (k < 4) mlo = fmaxf(mlo, m4);
+        else mhi = fmaxf(mhi, m4);
+      }
+      mlo = max_xor16(mlo) * score_scale;   // score_scale > 0
+      mhi = max_xor16(mhi) * score_scale;
+      const float tmax = max_xor32(fmaxf(mlo, mhi));
+      m_seen = fmaxf(m_seen, tmax);
+      if (m_ref == -INFINITY) m_ref = tmax;   // first tile of pass 0
+      overflow |= tmax > m_ref + kSlack;
+      const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
+      // block exponents: the block's largest weight maps to [128, 256)
+      int elo = mlo == -INFINITY ? 0 : (int)floorf(mlo - mbase);
+      int ehi = mhi == -INFINITY ? 0 : (int)floorf(mhi - mbase);
+      elo = elo < -100 ? -100 : (elo > 100 ? 100 : elo);
+      ehi = ehi < -100 ? -100 : (ehi > 100 ? 100 : ehi);
+      const float blo = mbase + (float)(elo - 7), bhi = mbase + (float)(ehi - 7);
+      i32x8 phi = {0, 0, 0, 0, 0, 0, 0, 0}, plo = {0, 0, 0, 0, 0, 0, 0, 0};
+      float slo = 0.f, shi = 0.f;
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        const float bsub = k < 4 ? blo : bhi;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
+        if (k < 4) slo += (p[0] + p[1]) + (p[2] + p[3]);
+        else shi += (p[0] + p[1]) + (p[2] + p[3]);
+        int hi, lo;
+        split_fp8x4(p[0], p[1], p[2], p[3], hi, lo);
+        phi[k] = hi;
+        plo[k] = lo;
+      }
+      l_part += slo * __uint_as_float((uint32_t)(127 + elo - 7) << 23) +
+                shi * __uint_as_float((uint32_t)(127 + ehi - 7) << 23);
+      // E8M0 scale operand: lane group 0 scales bytes 0-15 of groups {0,1},
+      // group 1 bytes 0-15 of {2,3}, group 2 bytes 16-31 of {0,1}, group 3
+      // bytes 16-31 of {2,3}.
+      const int epack = (elo + 120) | ((ehi + 120) << 8);
+      const int eother = partner_xor32(epack, lane);
+      const int psc = g == 0 ? (epack & 0xff)
+                    : g == 1 ? (eother & 0xff)
+                    : g == 2 ? (eother >> 8) : (epack >> 8);
+
+      // ---- O^T += V^T P^T over the tile (one 128-token operand per MFMA),
+      // V operands of the next column group prefetched.
+      auto load_v = [&](int j0, i32x8 (&vop)[kJ1]) {
+        int vaddr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vaddr[q] = ((j0 << 4) ^ vswz[q]) + vrow[q];
+#pragma unroll
+        for (int j1 = 0; j1 < kJ1; ++j1)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (DSA_LDS i32x2*)(vt + vaddr[q] + 256 * j1));
+            vop[j1][2 * q] = x.x;
+            vop[j1][2 * q + 1] = x.y;
+          }
+      };
+      i32x8 vbuf[2][kJ1];
+      load_v(0, vbuf[0]);
+#pragma unroll
+      for (int j0 = 0; j0 < kJ0; ++j0) {
+        if (j0 + 1 < kJ0) load_v(j0 + 1, vbuf[(j0 + 1) % 2]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j1 = 0; j1 < kJ1; ++j1) {
+          const int jd = 16 * j1 + j0;
+          O[jd] = mfma_fp8_pscaled(vbuf[j0 % 2][j1], phi, psc, O[jd]);
+          O[jd] = mfma_fp8_pscaled(vbuf[j0 % 2][j1], plo, psc, O[jd]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-
-    // ---- online softmax; lane holds head li, tokens 16*b + 4*g + i
-    const int tbase = it * kTileTokens;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kNB; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tbase + 16 * (tp + kTS * k) + 4 * g + i;
-        const float s = tok < n ? S[k][i] * a.scale_log2 : -INFINITY;
-        S[k][i] = s;
-        mx = fmaxf(mx, s);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int k = 0; k < kNB; ++k)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(S[k][i] - m_use);
-        S[k][i] = p;
-        psum += p;
-      }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int jd = 0; jd < kDBlocks; ++jd) O[jd] *= alpha;
-
-    // ---- O^T += V^T P^T, 32 tokens (two 16-token blocks) per MFMA
-#pragma unroll
-    for (int pp = 0; pp < (kNB + 1) / 2; ++pp) {
-      const int k0 = 2 * pp, k1 = 2 * pp + 1;
-      const bool has1 = k1 < kNB;
-      const int b0 = tp + kTS * k0;
-      const int b1 = has1 ? tp + kTS * k1 : b0;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = (__bf16)S[k0][e];
-        pb[4 + e] = has1 ? (__bf16)S[k1 < kNB ? k1 : k0][e] : (__bf16)0.f;
-      }
-      // transposing read: lanes 2k, 2k+1 of a 16-lane group address the two
-      // 8-byte halves of row k; lane li receives column li of all 8 rows.
-      const int krow = li >> 1;
-      const int vtok = (krow < 4 ? 16 * b0 : 16 * b1) + 4 * g + (krow & 3);
-      const int half = (li & 1) * 8;
-#pragma unroll
-      for (int jd = 0; jd < kDBlocks; ++jd) {
-        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (DSA_LDS i32x2*)(vt + tile_offset<D>(vtok, jd) + half));
-        O[jd] = mfma16(fp8x8_to_bf16x8((unsigned)raw.x, (unsigned)raw.y), pb, O[jd]);
-      }
+    // Recompute the chunk only if some wave saw a score beyond the slack.
+    if (pass == 0) {
+      if (__any(overflow) && lane == 0) redo_flag = 1;
+      __syncthreads();
+      const bool redo = redo_flag != 0;
+      __syncthreads();
+      if (!redo) break;
     }
   }
 
   // Sum of this head's weights over the four lane groups.
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  float l_run = l_part;
+  float l_run = sum_xor32(sum_xor16(l_part));
+  float m_run = ntiles > 0 ? m_ref : -INFINITY;
 
   // Waves that split the tokens of one head group merge (max, sum, O).
   if constexpr (kTS > 1) {
@@ -497,9 +713,9 @@ __global__ __launch_bounds__(256) void dsa_combine_kernel(CombineArgs a) {
 template <int D, int kTS>
 hipError_t launch_attend_ts(bool split_v, dim3 grid, hipStream_t st, const AttendArgs& args) {
   if (split_v)
-    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, true, 2>), grid, dim3(kThreads), 0, st, args);
+    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, true>), grid, dim3(kThreads), 0, st, args);
   else
-    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, false, 3>), grid, dim3(kThreads), 0, st, args);
+    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, false>), grid, dim3(kThreads), 0, st, args);
   return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@
 
 namespace dsa {
 
-// Tokens staged in LDS per pipeline step of the attend kernel.
-constexpr int kTileTokens = 64;
+// Granularity of a chunk (the selected tokens one attend workgroup takes).
+constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
 // Largest chunk one attend workgroup handles (its byte-offset table lives in
 // LDS: 2048 x 8 B = 16 KiB).
 constexpr int kMaxChunkTokens = 2048;

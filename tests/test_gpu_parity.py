@@ -369,3 +369,31 @@ def test_plan_on_gfx950_device(H):
     assert info["device"] == 0 and info["num_cus"] >= 1
     props = torch.cuda.get_device_properties(0)
     assert props.gcnArchName.startswith("gfx950")
+
+
+def test_score_far_above_the_first_tiles_max(H):
+    """A late token whose score exceeds every earlier one by hundreds of
+    log2 units: the weights must stay finite and the result match the
+    oracle (the softmax is then essentially one-hot on that token)."""
+    D, B, L = 512, 64, 1024
+    rng = np.random.default_rng(15)
+    pages = L // B
+    bt = rng.permutation(pages).astype(np.int32)[None, :]
+    pool = WL.fp8_codes_from_f32(rng.standard_normal(pages * B * D, dtype=np.float32) * 0.5)
+    big = 900
+    base = (bt[0, big // B] * B + big % B) * D
+    pool[base:base + D] = 0x7E           # 448 in every column
+    q = np.zeros((1, 16, D), np.float32)
+    q[0, :, :] = 8.0                      # large |q|: scores spread far
+    wl = WL.Workload(name="spread", rows=1, heads=16, D=D, block_size=B, kpool=4,
+                     width=L, bt_stride=pages, cache_stride_bytes=B * D, max_seq_len=L,
+                     num_pages=pages, sm_scale=1 / 16, k_scale=0.02, v_scale=0.02,
+                     sigma=1.0, seed=0, q_bits=WL.bf16_bits_from_f32(q),
+                     block_tables=bt, seq_lens=np.array([L], np.int32),
+                     sel=np.arange(L, dtype=np.int32)[None, :], pool=pool)
+    for ct in (0, 256):
+        _announce("score spread", chunk=ct)
+        run = H.run_gpu(wl, chunk_tokens=ct)
+        want = H.oracle_rows(wl, [0])
+        assert np.isfinite(run.out).all()
+        assert H.normwise_err(run.out, want).max() <= H.TOL
