@@ -72,7 +72,7 @@ typedef struct dsa_decode_params {
   int32_t block_table_stride;
   /* Bytes between consecutive pages of the cache; 0 selects
    * block_size * kv_lora_rank. Must be >= block_size * kv_lora_rank and a
-   * multiple of 16. */
+   * multiple of kv_lora_rank (latent rows are addressed by index). */
   uint64_t cache_stride_bytes;
   /* Upper bound on every seq_lens[r]; > 0. When block_table_stride > 0 it
    * must not exceed block_table_stride * block_size (a table row must cover
@@ -97,11 +97,12 @@ typedef struct dsa_decode_plan_s* dsa_decode_plan_t;
 /* Read-only description of a plan. */
 typedef struct dsa_decode_plan_info {
   int32_t device;          /* HIP device id, or -1 for a host-only plan */
-  int32_t chunk_tokens;    /* selected tokens per attend workgroup */
+  int32_t chunk_tokens;    /* selected tokens per workgroup */
   int32_t chunks_per_row;  /* workgroups per row per head block */
   int32_t head_blocks;     /* groups of up to 64 heads */
-  int32_t attend_workgroups;
-  int32_t uses_combine;    /* 1 when chunks_per_row > 1 */
+  int32_t workgroups;      /* rows * head_blocks * chunks_per_row */
+  int32_t merges_chunks;   /* 1 when chunks_per_row > 1: the last chunk of a
+                            * row to finish merges the others' partials */
   int32_t num_cus;         /* compute units the plan was sized for */
   int32_t reserved;
   uint64_t workspace_bytes;
@@ -123,9 +124,21 @@ int dsa_decode_plan(const dsa_decode_params* params, int device,
 void dsa_decode_plan_destroy(dsa_decode_plan_t plan);
 
 /* Device scratch bytes dsa_decode_launch needs (selection ids, token byte
- * offsets, per-row counts, and split partials when chunks_per_row > 1).
- * The caller allocates it; 0 for a NULL plan. */
+ * offsets, per-row counts, per-row arrival counters, and split partials when
+ * chunks_per_row > 1). The caller allocates it; 0 for a NULL plan. */
 size_t dsa_decode_workspace_bytes(dsa_decode_plan_t plan);
+
+/* Zero a workspace for `plan` on `stream` (a fill kernel, no memset, so it
+ * may be captured in a graph). Required once after the workspace is
+ * allocated, and again before it is used with a different plan: the arrival
+ * counters a launch relies on must start at zero. Every completed launch
+ * leaves them at zero again, so back-to-back launches (and graph replays)
+ * need no further initialisation. Zeroing the buffer any other way (e.g. a
+ * zero-filled allocation) is equivalent.
+ * Errors: DSA_DECODE_ERR_INVALID (NULL or host-only plan),
+ * DSA_DECODE_ERR_DEVICE, DSA_DECODE_ERR_WORKSPACE, DSA_DECODE_ERR_LAUNCH. */
+int dsa_decode_workspace_init(dsa_decode_plan_t plan, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /* Fill *info. DSA_DECODE_ERR_INVALID for a NULL argument. */
 int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info);
@@ -142,12 +155,15 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
  *   seq_lens     int32 [num_rows]
  *   sel_indices  int32 [num_rows, sel_width]
  *   out          bf16  [num_rows, num_q_heads, kv_lora_rank], 16-byte aligned
- *   workspace    >= dsa_decode_workspace_bytes(plan) bytes, 256-byte aligned;
+ *   workspace    >= dsa_decode_workspace_bytes(plan) bytes, 256-byte aligned,
+ *                zeroed once by dsa_decode_workspace_init for this plan;
  *                overwritten; must not be shared by launches in flight.
  * k_scale, v_scale: per-tensor dequantisation scales (finite).
  * Device-side preconditions (not checked by the kernels): every page id a
- * selected token maps to lies inside the pool; with block_table_stride 0 the
- * shared table has an entry for every position < max_seq_len.
+ * selected token maps to lies inside the pool; the pool holds fewer than
+ * 2^32 latent rows (page * cache_stride_bytes / kv_lora_rank + block_size
+ * < 2^32, i.e. under 2 TiB at kv_lora_rank 512); with block_table_stride 0
+ * the shared table has an entry for every position < max_seq_len.
  * Errors: DSA_DECODE_ERR_INVALID (NULL/misaligned pointer, host-only plan,
  * non-finite scale), DSA_DECODE_ERR_WORKSPACE, DSA_DECODE_ERR_LAUNCH. */
 int dsa_decode_launch(dsa_decode_plan_t plan, const void* q,
@@ -170,13 +186,13 @@ int dsa_decode_read_selection(dsa_decode_plan_t plan, const void* workspace,
                               size_t workspace_bytes, int32_t* ids,
                               int32_t* counts, uint64_t* offsets, void* stream);
 
-/* Per-kernel timing for benchmarks. dsa_decode_timing_begin makes the next
- * max_launches launches of this plan record HIP events around each kernel
- * on the launch stream (events are created here, not in the launch).
- * dsa_decode_timing_end waits for the recorded events and returns, summed
- * over the recorded launches, the milliseconds spent in the selection,
- * attend and combine kernels (kernel_ms[0..2]) and the number of launches
- * recorded; it then stops recording. */
+/* Kernel timing for benchmarks. dsa_decode_timing_begin makes the next
+ * max_launches launches of this plan record HIP events around the decode
+ * kernel on the launch stream (events are created here, not in the launch).
+ * dsa_decode_timing_end waits for the recorded events and returns in
+ * *kernel_ms the milliseconds spent in the decode kernel, summed over the
+ * recorded launches, and their number in *launches; it then stops
+ * recording. */
 int dsa_decode_timing_begin(dsa_decode_plan_t plan, int32_t max_launches);
 int dsa_decode_timing_end(dsa_decode_plan_t plan, float* kernel_ms,
                           int32_t* launches);
@@ -187,7 +203,7 @@ const char* dsa_decode_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 100
+#define DSA_DECODE_VERSION 200
 
 #ifdef __cplusplus
 }

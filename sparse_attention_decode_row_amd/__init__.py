@@ -9,7 +9,7 @@ the library is not built, every call raises.
     plan = Plan(num_rows=R, num_q_heads=H, kv_lora_rank=512, block_size=64,
                 index_kpool=4, sel_width=2048, block_table_stride=128,
                 max_seq_len=8192, sm_scale=1/16, device=0)
-    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    ws = plan.new_workspace()          # allocated and zeroed once
     plan.launch(q, cache, cache, block_tables, seq_lens, sel, k_scale, v_scale,
                 out, ws)
 """
@@ -30,7 +30,7 @@ DSA_DECODE_ERR_LAUNCH = -5
 
 EXPORTED_SYMBOLS = (
     "dsa_decode_plan", "dsa_decode_plan_destroy", "dsa_decode_workspace_bytes",
-    "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
+    "dsa_decode_workspace_init", "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
     "dsa_decode_timing_begin", "dsa_decode_timing_end", "dsa_decode_last_error",
     "dsa_decode_version",
 )
@@ -70,8 +70,8 @@ class PlanInfo(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("chunks_per_row", ctypes.c_int32),
         ("head_blocks", ctypes.c_int32),
-        ("attend_workgroups", ctypes.c_int32),
-        ("uses_combine", ctypes.c_int32),
+        ("workgroups", ctypes.c_int32),
+        ("merges_chunks", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_plan_destroy.argtypes = [vp]
         L.dsa_decode_workspace_bytes.restype = sz
         L.dsa_decode_workspace_bytes.argtypes = [vp]
+        L.dsa_decode_workspace_init.restype = ctypes.c_int
+        L.dsa_decode_workspace_init.argtypes = [vp, vp, sz, vp]
         L.dsa_decode_plan_get_info.restype = ctypes.c_int
         L.dsa_decode_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         L.dsa_decode_launch.restype = ctypes.c_int
@@ -180,6 +182,22 @@ class Plan:
     def workspace_bytes(self) -> int:
         return int(self._lib.dsa_decode_workspace_bytes(self.handle))
 
+    def workspace_init(self, workspace, workspace_bytes=None, stream=None) -> None:
+        """Zero `workspace` for this plan (once after allocation, and before
+        reusing it with another plan)."""
+        if workspace_bytes is None:
+            workspace_bytes = workspace.numel() * workspace.element_size()
+        _check(self._lib.dsa_decode_workspace_init(
+            self.handle, _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+    def new_workspace(self, device=None, stream=None):
+        """A torch uint8 device tensor of workspace_bytes, zeroed for this plan."""
+        import torch
+        dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+        ws = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        self.workspace_init(ws, stream=stream)
+        return ws
+
     def info(self) -> dict:
         inf = PlanInfo()
         _check(self._lib.dsa_decode_plan_get_info(self.handle, ctypes.byref(inf)))
@@ -207,11 +225,14 @@ class Plan:
     def timing_begin(self, max_launches: int) -> None:
         _check(self._lib.dsa_decode_timing_begin(self.handle, int(max_launches)))
 
-    def timing_end(self) -> Tuple[Tuple[float, float, float], int]:
-        ms = (ctypes.c_float * 3)()
+    def timing_end(self) -> Tuple[float, int]:
+        """(milliseconds in the decode kernel summed over the recorded
+        launches, number of launches recorded)."""
+        ms = ctypes.c_float()
         n = ctypes.c_int32()
-        _check(self._lib.dsa_decode_timing_end(self.handle, ms, ctypes.byref(n)))
-        return (float(ms[0]), float(ms[1]), float(ms[2])), int(n.value)
+        _check(self._lib.dsa_decode_timing_end(self.handle, ctypes.byref(ms),
+                                               ctypes.byref(n)))
+        return float(ms.value), int(n.value)
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:
@@ -237,7 +258,8 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
            cache_stride_bytes: int = 0, chunk_tokens: int = 0, out=None,
            workspace=None, stream=None):
     """One-shot helper: plan, allocate out/workspace with torch, launch.
-    q: bf16 [R, H, D] on the GPU; returns out (bf16 [R, H, D])."""
+    q: bf16 [R, H, D] on the GPU; returns out (bf16 [R, H, D]). A workspace
+    passed in must have been zeroed for this geometry (Plan.workspace_init)."""
     import torch
     R, H, D = q.shape
     plan = Plan(num_rows=R, num_q_heads=H, kv_lora_rank=D, block_size=block_size,
@@ -249,8 +271,7 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            workspace = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8,
-                                    device=q.device)
+            workspace = plan.new_workspace(q.device.index, stream=stream)
         plan.launch(q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
                     k_scale, v_scale, out, workspace, stream=stream)
     finally:

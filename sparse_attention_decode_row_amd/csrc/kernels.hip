@@ -1,63 +1,75 @@
-// gfx950 kernels and the launcher of the selected-index NoPE MLA paged decode.
+// gfx950 kernel and launcher of the selected-index NoPE MLA paged decode.
 //
 // What is computed is defined on the pages (cited by title):
 //   [attend]   "spark_model/layers/glm5next_dsa/attend.rs"
 //   [decode_k] "metrale_model_arch/glm5next_dsa/layer/decode_k.rs"
 //   [build]    "spark_model/layers/glm5next_dsa/build.rs"
-// How it is computed here is this library's own design for CDNA4 (wave64,
-// MFMA, 160 KiB LDS, LDS DMA, transposing LDS reads):
+// How it is computed is this library's own design for CDNA4 (wave64, FP8
+// matrix cores, 160 KiB LDS, LDS DMA, transposing LDS reads). One kernel does
+// the whole decode. A workgroup owns one (row, block of up to 64 heads, chunk
+// of the row's selected set) and runs two waves per 16-head group:
 //
-//   dsa_select_kernel   one workgroup per row: the selection row becomes a
-//                       set through an LDS bitmap over [0, seq_len) (holes,
-//                       repeats and out-of-range ids vanish; [attend] module
-//                       doc, "Why this is not the masked kernel"), read back
-//                       in ascending order, and every id is translated to the
-//                       byte offset of its FP8 latent row through the block
-//                       table ([decode_k] slot of a position).
-//   dsa_attend_kernel   one workgroup per (row, 64-head block, chunk of the
-//                       sorted set); 128-token tiles of latent rows are DMA'd
-//                       straight into LDS, double buffered. Each wave owns 16
-//                       heads. Both contractions run on the FP8 matrix cores
-//                       (16x16x128, fp32 accumulation) with the cached latent
-//                       bytes as they are, so nothing is converted per token:
-//                         S^T = K Q^T : Q (bf16) enters as an exact sum of two
-//                                       FP8 terms under a per-head power-of-two
-//                                       scale (8 significant bits = 4 + 4);
-//                         O^T = V^T P^T: the softmax weights enter as a sum of
-//                                       two FP8 terms (relative error <= 2^-9,
-//                                       below bf16's 2^-8); the V operand comes
-//                                       from ds_read_tr8_b64, which hands each
-//                                       lane 8 tokens of one latent column.
-//                       Online softmax in the exp2 domain. One chunk per row:
-//                       the BF16 output is written directly; several: fp32
-//                       partials plus (max, sum) per head.
-//   dsa_combine_kernel  merges the chunk partials of a row
-//                       (log-sum-exp weights) and writes BF16.
+//   1. selection   the row's ids become a set through an LDS bitmap over
+//                  [0, seq_len): holes, repeats and out-of-range ids vanish
+//                  ([attend] module doc, "Why this is not the masked kernel").
+//                  The workgroup keeps the ascending ids whose rank falls in
+//                  its chunk and translates each through the block table to
+//                  the index of its FP8 latent row ([decode_k], slot of a
+//                  position).
+//   2. gather      128-token tiles of latent rows are DMA'd straight from HBM
+//                  into LDS; the next tile is in flight while one is consumed.
+//   3. attend      both contractions run on the FP8 matrix cores (16x16x128,
+//                  fp32 accumulation) over the cached bytes as they are:
+//                    S^T = K Q^T   the two waves of a head group each score
+//                                  half of the tile's tokens. Q (bf16) enters
+//                                  as an exact sum of two FP8 terms under a
+//                                  per-head power-of-two scale;
+//                    O^T = V^T P^T each wave then accumulates half of the
+//                                  latent columns over all of the tile's
+//                                  tokens. The softmax weights enter as two
+//                                  FP8 terms (relative error <= 2^-9, below
+//                                  bf16's 2^-8) under per-block E8M0
+//                                  exponents, exchanged between the two waves
+//                                  through LDS; V comes from ds_read_b64_tr_b8,
+//                                  which hands each lane 8 tokens of one
+//                                  latent column.
+//                  Weights are taken against a fixed per-head reference (the
+//                  first tile's max); the block exponents absorb later
+//                  growth, so the accumulators are never rescaled.
+//   4. merge       one chunk: BF16 output directly. Several: fp32 partials
+//                  plus (reference, weight sum) per head, and the last chunk
+//                  of the row to finish merges them with log-sum-exp weights
+//                  ([attend], the split softmax and its combine).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <sstream>
-#include <type_traits>
 
 #include "plan.hpp"
 
 namespace dsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define DSA_LDS __attribute__((address_space(3)))
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
+constexpr int kTile = 128;  // tokens per staged tile (one PV operand's k extent)
 constexpr float kLog2e = 1.4426950408889634f;
+
+// How far (log2 domain) a score may exceed the per-head reference before the
+// chunk is recomputed against the exact maximum: weights up to 2^96 keep the
+// E8M0 block exponents in range and the fp32 sums (at most 2^96 * 448 * 2048
+// per element) finite.
+constexpr float kSlack = 96.0f;
 
 // ------------------------------------------------------------------ helpers
 
@@ -74,9 +86,18 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // D = 16x16 fp32 += A (16x128 FP8 E4M3) * B (128x16 FP8 E4M3). Lane l holds
-// A row l%16 and B column l%16, k = 32*(l/16) + [0, 32) as 32 bytes.
+// A row l%16 and B column l%16 as 32 bytes of the k dimension
+// (k = 32*(l/16) + byte).
 __device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Same with the B operand under per-lane E8M0 exponents (2^(byte - 127)).
+// Lane group 0 (lanes 0-15) scales bytes 0-15 of lane groups 0 and 1, group 1
+// bytes 0-15 of groups 2 and 3, group 2 bytes 16-31 of groups 0 and 1, group
+// 3 bytes 16-31 of groups 2 and 3 (each lane for its own column).
+__device__ __forceinline__ f32x4 mfma_fp8_bscaled(i32x8 a, i32x8 b, int bscale, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, bscale);
 }
 
 // Four floats -> four FP8 E4M3 codes (round to nearest even), byte i = x_i.
@@ -100,164 +121,25 @@ __device__ __forceinline__ void split_fp8x4(float x0, float x1, float x2, float 
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
+  return __uint_as_float((uint32_t)(127 + e) << 23);
+}
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// LDS layout of one staged tile: token-major rows of D bytes; the 16-byte
-// chunks of a row are XOR-permuted by the token index so that the 16 tokens
-// one MFMA operand read touches, and the 8 rows of one transposing read,
-// land in distinct bank groups.
-template <int D>
-__device__ __forceinline__ int tile_swizzle(int tok) {
-  constexpr int kChunks = D / 16;
-  constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
-  return ((tok & 15) ^ ((tok & 16) >> 1)) & kMask;
+// Device-coherent (agent-scope) scalar store / load: written through to, and
+// read from, the level shared by all XCDs, so the split partials leave no
+// dirty L2 lines for the release fence to write back.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int D>
-__device__ __forceinline__ int tile_offset(int tok, int chunk) {
-  return tok * D + ((chunk ^ tile_swizzle<D>(tok)) << 4);
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------- selection normalisation
-
-constexpr int kSelThreads = 256;
-constexpr int kWindowWords = 8192;   // 262144 positions per pass over the row
-constexpr int kSelIdsLds = 4096;     // sorted ids kept in LDS when W fits
-
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) sh[w] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int k = 0; k < kSelThreads / kWave; ++k) {
-    int s = sh[k];
-    all += s;
-    if (k < w) before += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
-}
-
-struct SelectArgs {
-  const int32_t* sel;
-  const int32_t* seq_lens;
-  const int32_t* block_tables;
-  int32_t* ids;
-  uint64_t* offsets;
-  int32_t* counts;
-  uint64_t cache_stride;
-  int width;
-  int max_seq_len;
-  int bt_stride;
-  int block_size;
-  int D;
-};
-
-__global__ __launch_bounds__(kSelThreads) void dsa_select_kernel(SelectArgs a) {
-  __shared__ uint32_t bitmap[kWindowWords];
-  __shared__ int32_t ids_lds[kSelIdsLds];
-  __shared__ int scan_sh[kSelThreads / kWave];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  int L = a.seq_lens[r];
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int32_t* srow = a.sel + (size_t)r * a.width;
-  const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
-  int32_t* idrow = a.ids + (size_t)r * a.width;
-  uint64_t* offrow = a.offsets + (size_t)r * a.width;
-  const bool ids_in_lds = a.width <= kSelIdsLds;
-
-  // Phase 1: membership bitmap per window of positions, read back in order.
-  int total = 0;
-  for (int base = 0; base < L; base += kWindowWords * 32) {
-    const int span = min(kWindowWords * 32, L - base);
-    const int nwords = (span + 31) >> 5;
-    for (int i = tid; i < nwords; i += kSelThreads) bitmap[i] = 0u;
-    __syncthreads();
-    // a hole (any negative id) or an id outside [0, L) sets nothing
-    for (int j = tid; j < a.width; j += kSelThreads) {
-      const int t = srow[j];
-      if (t >= base && t - base < span)
-        atomicOr(&bitmap[(t - base) >> 5], 1u << ((t - base) & 31));
-    }
-    __syncthreads();
-    const int per = (nwords + kSelThreads - 1) / kSelThreads;
-    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
-    int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
-    int blk_total;
-    int pos = total + block_exclusive_scan(cnt, scan_sh, &blk_total);
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = bitmap[w];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        const int t = base + (w << 5) + b;
-        if (ids_in_lds) ids_lds[pos] = t;
-        else idrow[pos] = t;
-        ++pos;
-      }
-    }
-    total += blk_total;
-    __syncthreads();
-  }
-
-  // Phase 2: ids in order -> byte offsets, four independent table lookups
-  // in flight per thread.
-  for (int i0 = tid; i0 < total; i0 += 4 * kSelThreads) {
-    int t[4];
-    uint32_t page[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kSelThreads;
-      t[u] = i < total ? (ids_in_lds ? ids_lds[i] : idrow[i]) : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      page[u] = i0 + u * kSelThreads < total ? (uint32_t)bt[t[u] / a.block_size] : 0u;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kSelThreads;
-      if (i < total) {
-        if (ids_in_lds) idrow[i] = t[u];
-        offrow[i] = (uint64_t)page[u] * a.cache_stride +
-                    (uint64_t)(t[u] % a.block_size) * (uint64_t)a.D;
-      }
-    }
-  }
-  if (tid == 0) a.counts[r] = total;
-}
-
-// ------------------------------------------------------------ gather-attend
-
-struct AttendArgs {
-  const uint16_t* q;
-  const uint8_t* k_cache;
-  const uint8_t* v_cache;
-  const int32_t* counts;
-  const uint64_t* offsets;
-  uint16_t* out;
-  float* part_o;
-  float* part_ml;
-  int H;
-  int width;
-  int chunks;
-  int chunk_tokens;
-  int head_blocks;
-  float scale_log2;  // sm_scale * k_scale * log2(e)
-  float v_scale;
-};
-
-// Value of the lane 16 (resp. 32) apart, and max-reductions over those lane
-// pairs, through the cross-row lane swaps (no LDS traffic).
+// Max / sum over lane pairs 16 (resp. 32) apart through the cross-row lane
+// swaps (no LDS traffic).
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
@@ -278,56 +160,121 @@ __device__ __forceinline__ float sum_xor32(float x) {
                                                   false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The value held by the lane 32 apart.
 __device__ __forceinline__ int partner_xor32(int x, int lane) {
   const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
   return (int)((lane & 32) ? r[0] : r[1]);
 }
 
-// O^T (16 latent columns x 16 heads) += V^T P^T over 128 tokens, with P given
-// as FP8 codes under per-block E8M0 exponents (scale_b) and V unscaled.
-__device__ __forceinline__ f32x4 mfma_fp8_pscaled(i32x8 v, i32x8 p, int pscale, f32x4 c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(v, p, c, 0, 0, 0, 127, 0, pscale);
+// LDS layout of one staged tile: slot-major rows of D bytes; the 16-byte
+// chunks of a row are XOR-permuted by the slot index so that the 16 rows one
+// MFMA operand read touches, and the 8 rows of one transposing read, land in
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int tile_swizzle(int slot) {
+  constexpr int kChunks = D / 16;
+  constexpr int kMask = (kChunks < 16 ? kChunks : 16) - 1;
+  return ((slot & 15) ^ ((slot & 16) >> 1)) & kMask;
 }
 
-// How far (log2 domain) a score may exceed the per-head reference before the
-// chunk is recomputed against the exact maximum: weights up to 2^96 keep the
-// E8M0 block exponents in range and the fp32 sums (at most 2^96 * 448 * 2048
-// per element) finite.
-constexpr float kSlack = 96.0f;
+// Exclusive prefix sum of one value per thread over the workgroup; *total
+// receives the sum over all threads.
+template <int kWaves>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) sh[w] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const int s = sh[k];
+    all += s;
+    if (k < w) before += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
 
-// kTS: waves that share one 16-head group and split each tile's tokens
-// (1 when the block has 64 heads, 2 for 32, 4 for 16 or fewer).
-// kSplitV: V is read from its own buffer (staged next to K).
-template <int D, int kTS, bool kSplitV>
-__global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
-  constexpr int kTile = kSplitV ? 64 : 128;         // tokens per stage
-  constexpr int kStages = 2;
-  constexpr int kKSteps = (D + 127) / 128;         // QK MFMA steps over the latent width
-  constexpr int kDBlocks = D / 16;                 // PV output column blocks
-  constexpr int kChunks = D / 16;                  // 16-byte chunks per latent row
-  constexpr int kChunkMask = (kChunks < 16 ? kChunks : 16) - 1;
-  constexpr int kJ0 = kDBlocks < 16 ? kDBlocks : 16;
-  constexpr int kJ1 = kDBlocks / kJ0;              // 2 when D = 512
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* sel;
+  uint16_t* out;
+  int32_t* ws_ids;       // [R, W] distinct ids, ascending (exported)
+  uint64_t* ws_offsets;  // [R, W] their latent-row byte offsets (exported)
+  int32_t* ws_counts;    // [R]
+  int32_t* ws_arrivals;  // [R * head_blocks] chunks finished; the merger resets it
+  float* part_o;         // [R, C, H, D]
+  float* part_ml;        // [R, C, H, 2]
+  uint32_t stride_rows;  // cache_stride_bytes / D
+  int H;
+  int width;
+  int max_seq_len;
+  int bt_stride;
+  int block_size;
+  int chunks;
+  int chunk_tokens;
+  int head_blocks;
+  float scale_log2;  // sm_scale * k_scale * log2(e), > 0
+  float v_scale;
+};
+
+// kGroups: 16-head groups per workgroup (1, 2 or 4); two waves per group.
+// kSplitV: V is read from its own buffer (K and V tiles staged side by side,
+// single-buffered, K of the next tile loading during PV and V during QK).
+// Otherwise K and V are the same bytes and the tile buffer is doubled.
+template <int D, int kGroups, bool kSplitV>
+__global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(DecodeArgs a) {
+  constexpr int kWaves = 2 * kGroups;
+  constexpr int kThreads = kWave * kWaves;
   constexpr int kTileBytes = kTile * D;
-  constexpr int kStageBytes = kTileBytes * (kSplitV ? 2 : 1);
-  constexpr int kLanesPerTok = D / 16;
+  constexpr int kSmemBytes = 2 * kTileBytes;        // two stages, or K + V
+  constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
+  constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
+  // PV: a wave accumulates kPair head groups over a 1/kCS slice of the
+  // latent columns, so each V operand read feeds 2*kPair MFMAs.
+  constexpr int kPair = kGroups >= 2 ? 2 : 1;
+  constexpr int kPairs = kGroups / kPair;           // PV head sets
+  constexpr int kCS = kWaves / kPairs;              // column slices
+  constexpr int kCB = kDBlocks / kCS;               // column blocks per PV wave
+  constexpr int kChunkMask = (kDBlocks < 16 ? kDBlocks : 16) - 1;
+  constexpr int kLanesPerTok = D / 16;              // DMA lanes per latent row
   constexpr int kTokPerInstr = kWave / kLanesPerTok;
-  constexpr int kInstrPerWave = kTileBytes / (kWave * 16) / kWaves;
-  constexpr int kGroups = kWaves / kTS;            // 16-head groups per workgroup
-  constexpr int kNB = kTile / 16 / kTS;            // 16-token blocks per wave per tile (<= 8)
-  constexpr int kSlotFloats = kDBlocks * 4 * kWave + 2 * kWave;
-  static_assert(kInstrPerWave >= 1, "tile too small for the DMA split");
-  static_assert(kNB >= 1 && kNB <= 8, "one PV operand covers 8 blocks of 16 tokens");
-  static_assert(kTS == 1 || 2 * kSlotFloats * 4 <= kStages * kStageBytes,
-                "merge scratch must fit in the tile buffers");
+  constexpr int kTPW = kTile / kWaves;              // tokens each wave DMAs per tile
+  constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per wave per tile
+  constexpr int kBitmapWords = kSmemBytes / 4;
+  static_assert(kInstr >= 1 && kInstr * kTokPerInstr == kTPW, "DMA split");
+  static_assert(kCB >= 1, "each wave needs at least one column block");
   static_assert(16 * 7 * D + 256 * ((kKSteps - 1) >> 1) < 65536,
                 "K operand offsets must fit the LDS instruction offset field");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
-  __shared__ uint64_t offs_lds[kMaxChunkTokens];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
+  // softmax weights of a tile, [group][hi|lo][token half][lane] x 4 blocks
+  __shared__ __attribute__((aligned(16))) i32x4 xch_p[kGroups][2][2][kWave];
+  __shared__ int xch_e[kGroups][2][kWave];   // their E8M0 exponent bytes
+  __shared__ float xch_f[kWaves][kWave];     // per-head scalars between the two waves
+  __shared__ float xch_m[kGroups][kWave];    // per-head reference, for the PV waves
+  __shared__ int scan_sh[kWaves];
+  __shared__ int flag_sh;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int g = lane >> 4, li = lane & 15;
+  // QK role: head group hg, token half hf of each tile. PV role: head groups
+  // pset*kPair + x (x < kPair), column blocks jbase .. jbase + kCB - 1.
+  const int hg = wave % kGroups, hf = wave / kGroups;
+  const int mate = hg + kGroups * (1 - hf);  // the other QK wave of the group
+  const int pset = wave % kPairs, jbase = (wave / kPairs) * kCB;
 
   int wg = blockIdx.x;
   const int c = wg % a.chunks;
@@ -335,47 +282,175 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
   const int hb = wg % a.head_blocks;
   const int r = wg / a.head_blocks;
 
-  const int hg = wave % kGroups, tp = wave / kGroups;
   const int head = hb * kHeadsPerBlock + hg * 16 + li;
   const bool head_ok = head < a.H;
 
-  const int n_row = a.counts[r];
-  const int cstart = c * a.chunk_tokens;
-  const int n = max(0, min(a.chunk_tokens, n_row - cstart));
-  const int ntiles = (n + kTile - 1) / kTile;
 
-  // Byte offsets of this chunk's rows, padded to whole tiles with the last
-  // real row (the padding is loaded but weighted by exactly zero).
-  const uint64_t* orow = a.offsets + (size_t)r * a.width + cstart;
-  for (int i = tid; i < ntiles * kTile; i += kThreads) offs_lds[i] = orow[min(i, n - 1)];
-
-  // ---- query slice of this lane: head li, latent columns 128*ks + 32*g + [0, 32)
-  // as two FP8 terms under a per-head power-of-two scale that puts the head's
-  // largest |q| in [128, 256).
-  i32x8 qhi[kKSteps], qlo[kKSteps];
-  float score_scale;
+  // ------------------------------------------------------------ 1. selection
+  // Membership bitmap over one window of positions at a time (the tile
+  // buffers are free until the first DMA). The workgroup keeps the ids of
+  // ascending rank cstart .. cend - 1.
+  const int cstart = c * a.chunk_tokens, cend = cstart + a.chunk_tokens;
+  const int32_t* srow = a.sel + (size_t)r * a.width;
+  // Loads in the order they are waited for (the counter drains in issue
+  // order): the length, a selection row of up to 4 ids per thread, then the
+  // query slice of this lane (head li, latent columns 128*ks + 32*g +
+  // [0, 32)), which is only needed after the selection.
+  int L = a.seq_lens[r];
+  const bool ids_in_regs = a.width <= 4 * kThreads;
+  int tpre[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = tid + u * kThreads;
+    tpre[u] = ids_in_regs && j < a.width ? srow[j] : -1;
+  }
+  u32x4 qraw[kKSteps][4];
   {
-    u32x4 raw[kKSteps][4];
-    float amax = 0.f;
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (head_ok ? head : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       const int d0 = 128 * ks + 32 * g;
       const bool ok = head_ok && d0 < D;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        raw[ks][v] = ok ? *(const u32x4*)(qrow + d0 + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+      for (int v = 0; v < 4; ++v)
+        qraw[ks][v] = ok ? *(const u32x4*)(qrow + d0 + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  uint32_t* bitmap = (uint32_t*)smem;
+  if (tid == 0) flag_sh = 0;
+  int total = 0;
+  for (int base = 0; base < L; base += kBitmapWords * 32) {
+    const int span = min(kBitmapWords * 32, L - base);
+    const int nwords = (span + 31) >> 5;
+    for (int i = tid; i < nwords; i += kThreads) bitmap[i] = 0u;
+    __syncthreads();
+    // a hole (any negative id) or an id outside [0, L) sets nothing
+    for (int j0 = tid; j0 < a.width; j0 += 4 * kThreads) {
+      int t[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * kThreads;
+        t[u] = ids_in_regs ? tpre[u] : (j < a.width ? srow[j] : -1);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (t[u] >= base && t[u] - base < span)
+          atomicOr(&bitmap[(t[u] - base) >> 5], 1u << ((t[u] - base) & 31));
+    }
+    __syncthreads();
+    const int per = (nwords + kThreads - 1) / kThreads;
+    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+    int blk_total;
+    int rank = total + block_exclusive_scan<kWaves>(cnt, scan_sh, &blk_total);
+    if (rank < cend && rank + cnt > cstart) {
+      for (int w = w0; w < w1 && rank < cend; ++w) {
+        uint32_t bits = bitmap[w];
+        while (bits && rank < cend) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          if (rank >= cstart) rows_lds[rank - cstart] = (uint32_t)(base + (w << 5) + b);
+          ++rank;
+        }
+      }
+    }
+    total += blk_total;
+    __syncthreads();
+  }
+  const int n = max(0, min(a.chunk_tokens, total - cstart));
+  const int ntiles = (n + kTile - 1) / kTile;
+
+  // ids -> latent row indices (page * rows per page + slot in page), four
+  // lookups in flight per thread. The head-block-0 workgroups of the row
+  // export the ids and byte offsets.
+  {
+    const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
+    const bool exporter = hb == 0;
+    int32_t* idw = a.ws_ids + (size_t)r * a.width + cstart;
+    uint64_t* offw = a.ws_offsets + (size_t)r * a.width + cstart;
+    for (int i0 = tid; i0 < n; i0 += 4 * kThreads) {
+      int t[4];
+      uint32_t page[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        t[u] = i0 + u * kThreads < n ? (int)rows_lds[i0 + u * kThreads] : 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        page[u] = i0 + u * kThreads < n ? (uint32_t)bt[t[u] / a.block_size] : 0u;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kThreads;
+        if (i < n) {
+          const uint32_t row = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
+          rows_lds[i] = row;
+          if (exporter) {
+            idw[i] = t[u];
+            offw[i] = (uint64_t)row * (uint64_t)D;
+          }
+        }
+      }
+    }
+    if (c == 0 && hb == 0 && tid == 0) a.ws_counts[r] = total;
+    __syncthreads();
+    // pad to whole tiles with the last real row (loaded, weighted by zero)
+    if (n > 0)
+      for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
+    __syncthreads();
+  }
+
+  // -------------------------------------------------------------- 2. gather
+  // Wave w moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its instruction k
+  // writes kTokPerInstr consecutive LDS slots; DMA lane l carries chunk
+  // l % kLanesPerTok of token w*kTPW + (l / kLanesPerTok)*kInstr + k, so a
+  // lane's kInstr row indices are contiguous in the row table.
+  DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
+  const DSA_LDS uint32_t* rows_l = (const DSA_LDS uint32_t*)rows_lds;
+  auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
+    const int j = lane / kLanesPerTok, ci = lane % kLanesPerTok;
+    const DSA_LDS uint32_t* rr = rows_l + tile * kTile + wave * kTPW + j * kInstr;
+    uint32_t row[kInstr];
+#pragma unroll
+    for (int k = 0; k < kInstr; ++k) row[k] = rr[k];
+#pragma unroll
+    for (int k = 0; k < kInstr; ++k) {
+      const int slot0 = wave * kTPW + k * kTokPerInstr;
+      const int swz = tile_swizzle<D>(slot0 + j);
+      const uint64_t off = (uint64_t)row[k] * (uint64_t)D + (uint64_t)((ci ^ swz) << 4);
+      __builtin_amdgcn_global_load_lds(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D),
+                                       16, 0, 0);
+    }
+  };
+  // Token index (within the tile) held by LDS slot s.
+  auto token_of_slot = [&](int s) {
+    const int w = s / kTPW, sw = s % kTPW;
+    return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
+  };
+  if (ntiles > 0) {
+    issue_tile(0, 0, a.k_cache);
+    if constexpr (kSplitV) issue_tile(0, kTileBytes, a.v_cache);
+  }
+
+  // ---- the query slice as two FP8 terms under a per-head power-of-two
+  // scale that puts the head's largest |q| in [128, 256)
+  i32x8 qhi[kKSteps], qlo[kKSteps];
+  float score_scale;
+  {
+    const auto& raw = qraw;
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[ks][v][e])), fabsf(bf16_hi(raw[ks][v][e]))));
-      }
-    }
     amax = max_xor32(max_xor16(amax));
-    int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
+    const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
     int sh = 7 - e;
     sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
-    const float qs = __uint_as_float((uint32_t)(127 + sh) << 23);       // 2^sh
-    const float qs_inv = __uint_as_float((uint32_t)(127 - sh) << 23);   // 2^-sh
+    const float qs = pow2i(sh);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
 #pragma unroll
@@ -389,95 +464,81 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
           qhi[ks][2 * v + h2] = hi;
           qlo[ks][2 * v + h2] = lo;
         }
-    score_scale = a.scale_log2 * qs_inv;
+    score_scale = a.scale_log2 * pow2i(-sh);
   }
-  __syncthreads();
 
-  auto issue_tile = [&](int tile, int stage) {
-    uint8_t* sbase = smem + stage * kStageBytes;
-#pragma unroll
-    for (int k = 0; k < kInstrPerWave; ++k) {
-      const int gi = wave * kInstrPerWave + k;
-      const int tt = gi * kTokPerInstr + lane / kLanesPerTok;
-      const int ci = lane % kLanesPerTok;
-      const uint64_t off = offs_lds[tile * kTile + tt] +
-                           (uint64_t)((ci ^ tile_swizzle<D>(tt)) << 4);
-      __builtin_amdgcn_global_load_lds(a.k_cache + off,
-                                       (DSA_LDS void*)(sbase + gi * (kWave * 16)),
-                                       16, 0, 0);
-      if constexpr (kSplitV)
-        __builtin_amdgcn_global_load_lds(
-            a.v_cache + off, (DSA_LDS void*)(sbase + kTileBytes + gi * (kWave * 16)),
-            16, 0, 0);
-    }
-  };
-
-  // K operand addresses. Token 16*b + li, chunk 8*ks + 2*g + h sits at chunk
-  // position (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position is
-  // 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ b) & 1)), so four per-lane
+  // K operand addresses. This wave scores blocks b = 4*hf + k (k < 4) of 16
+  // slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk position
+  // (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position is
+  // 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ k) & 1)), so four per-lane
   // offsets plus compile-time immediates cover every read.
   int kofs[2][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      kofs[p][h] = li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
+      kofs[p][h] = 64 * D * hf + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
 
   // V operand rows: read q (0..3) of a PV operand covers operand bytes
-  // 8q..8q+7, i.e. block slots 2q and 2q+1; lanes 2k and 2k+1 of a 16-lane
-  // group supply row k (halves 0 and 1).
+  // 8q..8q+7, i.e. blocks 2q and 2q+1; lanes 2k and 2k+1 of a 16-lane group
+  // supply row k (halves 0 and 1).
   int vrow[4], vswz[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int rrow = li >> 1;
-    const int slot = 2 * q + (rrow >> 2);
-    const int b = slot < kNB ? tp + kTS * slot : tp;   // slots past this wave's blocks weigh zero
-    const int tok = 16 * b + 4 * g + (rrow & 3);
-    vrow[q] = tok * D + 8 * (li & 1);
-    vswz[q] = tile_swizzle<D>(tok) << 4;
+    const int slot = 16 * (2 * q + (rrow >> 2)) + 4 * g + (rrow & 3);
+    vrow[q] = slot * D + 8 * (li & 1);
+    vswz[q] = tile_swizzle<D>(slot) << 4;
   }
 
+  // -------------------------------------------------------------- 3. attend
   // The accumulators are touched only by the matrix cores inside the tile
-  // loop: softmax weights are taken against a fixed per-head reference (the
-  // first tile's max). Each 16-token x 2-lane-group block of weights carries
+  // loop: weights are taken against a fixed per-head reference (the first
+  // tile's max), and each 16-token x 2-lane-group block of weights carries
   // its own E8M0 exponent, so a later score may exceed the reference by up
   // to 2^kSlack without leaving the FP8 range or fp32 accumulation. Should a
   // score ever exceed it by more (only with pathological inputs), the chunk
   // is recomputed with the reference set to the exact maximum seen.
-  DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
-  __shared__ int redo_flag;
-  f32x4 O[kDBlocks];
-  float l_part = 0.f;       // this lane's share of sum_t 2^(s_t - m_ref)
-  float m_ref = -INFINITY;  // reference of this head's scores (log2 domain)
-  float m_seen = -INFINITY; // exact max of this head's scores so far
+  f32x4 O[kPair][kCB];
+  float l_part = 0.f;        // this lane's share of sum_t 2^(s_t - m_ref)
+  float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
+  float m_seen = -INFINITY;  // exact max of this wave's scores so far
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int jd = 0; jd < kDBlocks; ++jd) O[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < kPair; ++x)
+#pragma unroll
+      for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
-    if (pass == 1) m_ref = m_seen;
     bool overflow = false;
-    if (tid == 0) redo_flag = 0;
+    if (pass == 1 && ntiles > 0) {
+      issue_tile(0, 0, a.k_cache);
+      if constexpr (kSplitV) issue_tile(0, kTileBytes, a.v_cache);
+    }
 
-    if (ntiles > 0) issue_tile(0, 0);
     for (int it = 0; it < ntiles; ++it) {
       wait_vmcnt<0>();
-      barrier_lds();  // tile `it` is in LDS for every wave; tile it-1 is consumed
-      if (it + 1 < ntiles) issue_tile(it + 1, (it + 1) % kStages);
+      barrier_lds();  // tile `it` (its K half when split) is in LDS; PV of it-1 is done
+      int koff, voff;
+      if constexpr (kSplitV) {
+        koff = 0;
+        voff = kTileBytes;
+        if (it > 0) issue_tile(it, kTileBytes, a.v_cache);  // V buffer is free again
+      } else {
+        koff = voff = (it & 1) * kTileBytes;
+        if (it + 1 < ntiles) issue_tile(it + 1, ((it + 1) & 1) * kTileBytes, a.k_cache);
+      }
 
-      const int stage_off = (it % kStages) * kStageBytes;
-      const DSA_LDS uint8_t* kt = lds + stage_off;
-      const DSA_LDS uint8_t* vt = kSplitV ? kt + kTileBytes : kt;
-
-      // ---- S^T = K Q^T, K operands prefetched two MFMA steps ahead
-      constexpr int kSteps = kNB * kKSteps;
+      // ---- S^T = K Q^T over this wave's four blocks, K operands prefetched
+      // two MFMA steps ahead
+      const DSA_LDS uint8_t* kt = lds + koff;
+      constexpr int kSteps = 4 * kKSteps;
       auto load_k = [&](int s) -> i32x8 {
         const int k = s / kKSteps, ks = s % kKSteps;
-        const int b = tp + kTS * k;
         i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
         if (128 * ks + 32 * g < D) {
-          const int p = (ks ^ b) & 1;
-          const DSA_LDS uint8_t* base = kt + 16 * b * D + 256 * (ks >> 1);
+          const int p = (ks ^ k) & 1;
+          const DSA_LDS uint8_t* base = kt + 16 * k * D + 256 * (ks >> 1);
           const u32x4 lo = *(const DSA_LDS u32x4*)(base + kofs[p][0]);
           const u32x4 hi = *(const DSA_LDS u32x4*)(base + kofs[p][1]);
           kop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
@@ -485,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
         }
         return kop;
       };
-      f32x4 S[kNB];
+      f32x4 S[4];
       i32x8 kbuf[3];
       kbuf[0] = load_k(0);
       if (kSteps > 1) kbuf[1] = load_k(1);
@@ -500,252 +561,297 @@ __global__ __launch_bounds__(kThreads, 1) void dsa_attend_kernel(AttendArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- weights; lane holds head li, tokens 16*b + 4*g + i. Slots 0-3 and
-      // 4-7 of the lane, each joined with the lane 16 apart, are the blocks
-      // that share one FP8 exponent.
+      // ---- weights. The lane holds head li at slots 16*(4*hf + k) + 4*g + i;
+      // joined with the lane 16 apart these 16 x 2 weights share one FP8
+      // exponent (operand bytes 16*hf .. 16*hf + 15 of lane groups g, g^1).
       const int nvalid = n - it * kTile;
       if (__builtin_expect(nvalid < kTile, 0)) {
 #pragma unroll
-        for (int k = 0; k < kNB; ++k)
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (16 * (tp + kTS * k) + 4 * g + i >= nvalid) S[k][i] = -INFINITY;
+            if (token_of_slot(16 * (4 * hf + k) + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
       }
-      float mlo = -INFINITY, mhi = -INFINITY;
+      float mh = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        const float m4 = fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3]));
-        if (k < 4) mlo = fmaxf(mlo, m4);
-        else mhi = fmaxf(mhi, m4);
-      }
-      mlo = max_xor16(mlo) * score_scale;   // score_scale > 0
-      mhi = max_xor16(mhi) * score_scale;
-      const float tmax = max_xor32(fmaxf(mlo, mhi));
+      for (int k = 0; k < 4; ++k)
+        mh = fmaxf(mh, fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3])));
+      mh = max_xor16(mh) * score_scale;  // score_scale > 0
+      const float tmax = max_xor32(mh);
       m_seen = fmaxf(m_seen, tmax);
-      if (m_ref == -INFINITY) m_ref = tmax;   // first tile of pass 0
+      if (pass == 0 && it == 0) {
+        // first tile: the reference is the tile's max over both halves of
+        // the head group (a workgroup-uniform branch: it holds a barrier)
+        xch_f[wave][lane] = tmax;
+        barrier_lds();
+        m_ref = fmaxf(tmax, xch_f[mate][lane]);
+      }
       overflow |= tmax > m_ref + kSlack;
       const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
-      // block exponents: the block's largest weight maps to [128, 256)
-      int elo = mlo == -INFINITY ? 0 : (int)floorf(mlo - mbase);
-      int ehi = mhi == -INFINITY ? 0 : (int)floorf(mhi - mbase);
-      elo = elo < -100 ? -100 : (elo > 100 ? 100 : elo);
-      ehi = ehi < -100 ? -100 : (ehi > 100 ? 100 : ehi);
-      const float blo = mbase + (float)(elo - 7), bhi = mbase + (float)(ehi - 7);
-      i32x8 phi = {0, 0, 0, 0, 0, 0, 0, 0}, plo = {0, 0, 0, 0, 0, 0, 0, 0};
-      float slo = 0.f, shi = 0.f;
+      // block exponent: the block's largest weight maps to [128, 256)
+      int e = mh == -INFINITY ? 0 : (int)floorf(mh - mbase);
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+      const float bsub = mbase + (float)(e - 7);
+      i32x4 phi, plo;
+      float lsum = 0.f;
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) {
-        const float bsub = k < 4 ? blo : bhi;
+      for (int k = 0; k < 4; ++k) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
-        if (k < 4) slo += (p[0] + p[1]) + (p[2] + p[3]);
-        else shi += (p[0] + p[1]) + (p[2] + p[3]);
+        lsum += (p[0] + p[1]) + (p[2] + p[3]);
         int hi, lo;
         split_fp8x4(p[0], p[1], p[2], p[3], hi, lo);
         phi[k] = hi;
         plo[k] = lo;
       }
-      l_part += slo * __uint_as_float((uint32_t)(127 + elo - 7) << 23) +
-                shi * __uint_as_float((uint32_t)(127 + ehi - 7) << 23);
-      // E8M0 scale operand: lane group 0 scales bytes 0-15 of groups {0,1},
-      // group 1 bytes 0-15 of {2,3}, group 2 bytes 16-31 of {0,1}, group 3
-      // bytes 16-31 of {2,3}.
-      const int epack = (elo + 120) | ((ehi + 120) << 8);
-      const int eother = partner_xor32(epack, lane);
-      const int psc = g == 0 ? (epack & 0xff)
-                    : g == 1 ? (eother & 0xff)
-                    : g == 2 ? (eother >> 8) : (epack >> 8);
+      l_part += lsum * pow2i(e - 7);
+      xch_p[hg][0][hf][lane] = phi;
+      xch_p[hg][1][hf][lane] = plo;
+      xch_e[hg][hf][lane] = e + 120;
 
-      // ---- O^T += V^T P^T over the tile (one 128-token operand per MFMA),
-      // V operands of the next column group prefetched.
-      auto load_v = [&](int j0, i32x8 (&vop)[kJ1]) {
-        int vaddr[4];
+      if constexpr (kSplitV) {
+        wait_vmcnt<0>();  // V of this tile
+        barrier_lds();    // every wave's V rows landed, K reads done, weights visible
+        if (it + 1 < ntiles) issue_tile(it + 1, 0, a.k_cache);
+      } else {
+        barrier_lds();    // weights visible (the next tile stays in flight)
+      }
+
+      // ---- full P^T operands of this wave's head groups and their exponents
+      i32x8 pH[kPair], pL[kPair];
+      int psc[kPair];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) vaddr[q] = ((j0 << 4) ^ vswz[q]) + vrow[q];
+      for (int x = 0; x < kPair; ++x) {
+        const int hx = pset * kPair + x;
+        const i32x4 h0 = xch_p[hx][0][0][lane], h1 = xch_p[hx][0][1][lane];
+        const i32x4 l0 = xch_p[hx][1][0][lane], l1 = xch_p[hx][1][1][lane];
+        pH[x] = i32x8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        pL[x] = i32x8{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+        const int epack = xch_e[hx][0][lane] | (xch_e[hx][1][lane] << 8);
+        const int eother = partner_xor32(epack, lane);
+        psc[x] = g == 0 ? (epack & 0xff)
+               : g == 1 ? (eother & 0xff)
+               : g == 2 ? (eother >> 8) : (epack >> 8);
+      }
+
+      // ---- O^T += V^T P^T over this wave's column blocks (one 128-token
+      // operand per MFMA, shared by the head groups), V operands of the next
+      // block prefetched.
+      const DSA_LDS uint8_t* vt = lds + voff;
+      auto load_v = [&](int j0) -> i32x8 {
+        i32x8 vop;
 #pragma unroll
-        for (int j1 = 0; j1 < kJ1; ++j1)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (DSA_LDS i32x2*)(vt + vaddr[q] + 256 * j1));
-            vop[j1][2 * q] = x.x;
-            vop[j1][2 * q + 1] = x.y;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int addr = (((jbase + j0) << 4) ^ vswz[q]) + vrow[q];
+          const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
+          vop[2 * q] = v2.x;
+          vop[2 * q + 1] = v2.y;
+        }
+        return vop;
       };
-      i32x8 vbuf[2][kJ1];
-      load_v(0, vbuf[0]);
+      i32x8 vbuf[2];
+      vbuf[0] = load_v(0);
 #pragma unroll
-      for (int j0 = 0; j0 < kJ0; ++j0) {
-        if (j0 + 1 < kJ0) load_v(j0 + 1, vbuf[(j0 + 1) % 2]);
+      for (int j0 = 0; j0 < kCB; ++j0) {
+        if (j0 + 1 < kCB) vbuf[(j0 + 1) & 1] = load_v(j0 + 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j1 = 0; j1 < kJ1; ++j1) {
-          const int jd = 16 * j1 + j0;
-          O[jd] = mfma_fp8_pscaled(vbuf[j0 % 2][j1], phi, psc, O[jd]);
-          O[jd] = mfma_fp8_pscaled(vbuf[j0 % 2][j1], plo, psc, O[jd]);
-        }
+        for (int x = 0; x < kPair; ++x)
+          O[x][j0] = mfma_fp8_bscaled(vbuf[j0 & 1], pH[x], psc[x], O[x][j0]);
+#pragma unroll
+        for (int x = 0; x < kPair; ++x)
+          O[x][j0] = mfma_fp8_bscaled(vbuf[j0 & 1], pL[x], psc[x], O[x][j0]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Recompute the chunk only if some wave saw a score beyond the slack.
     if (pass == 0) {
-      if (__any(overflow) && lane == 0) redo_flag = 1;
+      if (__any(overflow) && lane == 0) flag_sh = 1;
+      xch_f[wave][lane] = m_seen;
       __syncthreads();
-      const bool redo = redo_flag != 0;
+      const bool redo = flag_sh != 0;
+      if (redo) m_ref = fmaxf(m_seen, xch_f[mate][lane]);
       __syncthreads();
       if (!redo) break;
     }
   }
 
-  // Sum of this head's weights over the four lane groups.
-  float l_run = sum_xor32(sum_xor16(l_part));
-  float m_run = ntiles > 0 ? m_ref : -INFINITY;
-
-  // Waves that split the tokens of one head group merge (max, sum, O).
-  if constexpr (kTS > 1) {
-    __syncthreads();  // tiles fully consumed; no DMA outstanding
-    float* scratch = (float*)smem;
+  // Weight sums and references of the PV waves' heads (both token halves).
+  xch_f[wave][lane] = sum_xor32(sum_xor16(l_part));
+  if (hf == 0) xch_m[hg][lane] = ntiles > 0 ? m_ref : -INFINITY;
+  __syncthreads();
+  float l_run[kPair], m_run[kPair];
 #pragma unroll
-    for (int step = kTS / 2; step >= 1; step /= 2) {
-      if (tp >= step && tp < 2 * step) {
-        float* slot = scratch + (hg * step + (tp - step)) * kSlotFloats;
-#pragma unroll
-        for (int jd = 0; jd < kDBlocks; ++jd)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) slot[(jd * 4 + i) * kWave + lane] = O[jd][i];
-        slot[kDBlocks * 4 * kWave + lane] = m_run;
-        slot[kDBlocks * 4 * kWave + kWave + lane] = l_run;
-      }
-      __syncthreads();
-      if (tp < step) {
-        const float* slot = scratch + (hg * step + tp) * kSlotFloats;
-        const float mb = slot[kDBlocks * 4 * kWave + lane];
-        const float lb = slot[kDBlocks * 4 * kWave + kWave + lane];
-        const float mn = fmaxf(m_run, mb);
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        const float fa = fast_exp2(m_run - mu), fb = fast_exp2(mb - mu);
-#pragma unroll
-        for (int jd = 0; jd < kDBlocks; ++jd)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            O[jd][i] = O[jd][i] * fa + slot[(jd * 4 + i) * kWave + lane] * fb;
-        l_run = l_run * fa + lb * fb;
-        m_run = mn;
-      }
-      __syncthreads();
-    }
+  for (int x = 0; x < kPair; ++x) {
+    const int hx = pset * kPair + x;
+    l_run[x] = xch_f[hx][lane] + xch_f[hx + kGroups][lane];
+    m_run[x] = xch_m[hx][lane];
   }
 
-  if (tp != 0 || !head_ok) return;
-  // Lane holds O^T rows d = 16*jd + 4*g + i for head li.
+  // --------------------------------------------------------------- 4. merge
+  // Lane holds O^T rows d = 16*(jbase + j) + 4*g + i for head li of group
+  // pset*kPair + x.
+  auto store_out = [&](int x, const f32x4* o, float lsum) {
+    const int hx = hb * kHeadsPerBlock + (pset * kPair + x) * 16 + li;
+    if (hx >= a.H) return;
+    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+    uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+      const bf16x4 v = {(__bf16)(o[j][0] * inv), (__bf16)(o[j][1] * inv),
+                        (__bf16)(o[j][2] * inv), (__bf16)(o[j][3] * inv)};
+      *(bf16x4*)(orow + 16 * (jbase + j) + 4 * g) = v;
+    }
+  };
   if (a.chunks == 1) {
-    const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
-    uint16_t* orow_out = a.out + ((size_t)r * a.H + head) * D;
 #pragma unroll
-    for (int jd = 0; jd < kDBlocks; ++jd) {
-      bf16x4 v = {(__bf16)(O[jd][0] * inv), (__bf16)(O[jd][1] * inv),
-                  (__bf16)(O[jd][2] * inv), (__bf16)(O[jd][3] * inv)};
-      *(bf16x4*)(orow_out + 16 * jd + 4 * g) = v;
-    }
-  } else {
-    const size_t ph = ((size_t)r * a.chunks + c) * a.H + head;
-    float* po = a.part_o + ph * D;
+    for (int x = 0; x < kPair; ++x) store_out(x, O[x], l_run[x]);
+    return;
+  }
+  // Partials of a workgroup: each wave's accumulators as they sit in its
+  // registers, component-major (256 contiguous bytes per store), then
+  // (reference, sum) of the block's 64 heads; all device-coherent.
+  constexpr int kPartFloats = kPair * kCB * kWave * 4;  // per wave
+  const size_t wg_slot = (size_t)(r * a.head_blocks + hb) * a.chunks;
+  auto part_o_of = [&](int cc) {
+    return a.part_o + ((wg_slot + cc) * kWaves + wave) * kPartFloats;
+  };
+  auto part_ml_of = [&](int cc, int x) {
+    return a.part_ml + ((wg_slot + cc) * kHeadsPerBlock + (pset * kPair + x) * 16 + li) * 2;
+  };
+  {
+    float* po = part_o_of(c);
 #pragma unroll
-    for (int jd = 0; jd < kDBlocks; ++jd) *(f32x4*)(po + 16 * jd + 4 * g) = O[jd];
-    if (g == 0) {
-      a.part_ml[ph * 2 + 0] = m_run;
-      a.part_ml[ph * 2 + 1] = l_run;
+    for (int x = 0; x < kPair; ++x)
+#pragma unroll
+      for (int j = 0; j < kCB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_dev(po + ((x * kCB + j) * 4 + i) * kWave + lane, O[x][j][i]);
+    if (jbase == 0 && g == 0)
+#pragma unroll
+      for (int x = 0; x < kPair; ++x) {
+        float* pml = part_ml_of(c, x);
+        store_dev(pml, m_run[x]);
+        store_dev(pml + 1, l_run[x]);
+      }
+  }
+  // The last chunk of this (row, head block) to arrive merges all chunks.
+  // The workgroup barrier orders every wave's partial stores before thread
+  // 0's device-scope release (one L2 write-back per workgroup, not one per
+  // wave); thread 0's acquire after the count likewise covers the loads the
+  // other waves issue after the second barrier.
+  __syncthreads();
+  if (tid == 0) {
+    int32_t* ctr = &a.ws_arrivals[r * a.head_blocks + hb];
+    __threadfence();
+    const int old = atomicAdd(ctr, 1);
+    const bool last = old == a.chunks - 1;
+    if (last) {
+      *ctr = 0;  // ready for the next launch
+      __threadfence();
     }
+    flag_sh = last ? 2 : 0;
+  }
+  __syncthreads();
+  if (flag_sh != 2) return;
+  // Fixed chunk order, whichever chunk merges, so the result is deterministic.
+#pragma unroll
+  for (int x = 0; x < kPair; ++x) {
+    float M = m_run[x];
+    for (int cc = 0; cc < a.chunks; ++cc)
+      if (cc != c) M = fmaxf(M, load_dev(part_ml_of(cc, x)));
+    f32x4 acc[kCB];
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float Lsum = 0.f;
+    if (M != -INFINITY) {
+      for (int cc = 0; cc < a.chunks; ++cc) {
+        const float* pml = part_ml_of(cc, x);
+        const float mc = cc == c ? m_run[x] : load_dev(pml);
+        if (mc == -INFINITY) continue;  // empty chunk: its partial is zero
+        const float w = fast_exp2(mc - M);
+        Lsum += w * (cc == c ? l_run[x] : load_dev(pml + 1));
+        if (cc == c) {
+#pragma unroll
+          for (int j = 0; j < kCB; ++j) acc[j] += w * O[x][j];
+        } else {
+          const float* po = part_o_of(cc);
+#pragma unroll
+          for (int j = 0; j < kCB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[j][i] += w * load_dev(po + ((x * kCB + j) * 4 + i) * kWave + lane);
+        }
+      }
+    }
+    store_out(x, acc, Lsum);
   }
 }
 
-// ------------------------------------------------------------------ combine
-
-struct CombineArgs {
-  const float* part_o;
-  const float* part_ml;
-  uint16_t* out;
-  int H;
-  int chunks;
-  int head_groups;  // blocks of kCombineHeads per row
-  float v_scale;
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void dsa_combine_kernel(CombineArgs a) {
-  constexpr int kTPH = D / 8;        // threads per head, 8 columns each
-  constexpr int kHPB = 256 / kTPH;   // heads per workgroup
-  const int r = blockIdx.x / a.head_groups;
-  const int head = (blockIdx.x % a.head_groups) * kHPB + threadIdx.x / kTPH;
-  if (head >= a.H) return;
-  const int d0 = (threadIdx.x % kTPH) * 8;
-  float M = -INFINITY;
-  for (int c = 0; c < a.chunks; ++c)
-    M = fmaxf(M, a.part_ml[(((size_t)r * a.chunks + c) * a.H + head) * 2]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int c = 0; c < a.chunks; ++c) {
-      const size_t ph = ((size_t)r * a.chunks + c) * a.H + head;
-      const float mc = a.part_ml[ph * 2];
-      if (mc == -INFINITY) continue;  // empty chunk: nothing was written
-      const float w = fast_exp2(mc - M);
-      L += w * a.part_ml[ph * 2 + 1];
-      const f32x4 x0 = *(const f32x4*)(a.part_o + ph * D + d0);
-      const f32x4 x1 = *(const f32x4*)(a.part_o + ph * D + d0 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += w * x0[i];
-        acc[4 + i] += w * x1[i];
-      }
-    }
-  }
-  const float inv = L > 0.f ? a.v_scale / L : 0.f;
-  bf16x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
-  *(bf16x8*)(a.out + ((size_t)r * a.H + head) * D + d0) = v;
+// Zero a word range (workspace set-up; a kernel rather than a memset so that
+// it can sit in a captured graph).
+__global__ void dsa_zero_kernel(int32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
 }
 
 // ------------------------------------------------------------------ launch
 
-template <int D, int kTS>
-hipError_t launch_attend_ts(bool split_v, dim3 grid, hipStream_t st, const AttendArgs& args) {
+template <int D, int kGroups>
+hipError_t launch_g(bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+  const dim3 block(2 * kGroups * kWave);
   if (split_v)
-    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, true>), grid, dim3(kThreads), 0, st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
   else
-    hipLaunchKernelGGL((dsa_attend_kernel<D, kTS, false>), grid, dim3(kThreads), 0, st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false>), grid, block, 0, st, args);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_attend_d(int ts, bool split_v, dim3 grid, hipStream_t st,
-                           const AttendArgs& args) {
-  switch (ts) {
-    case 1: return launch_attend_ts<D, 1>(split_v, grid, st, args);
-    case 2: return launch_attend_ts<D, 2>(split_v, grid, st, args);
-    default: return launch_attend_ts<D, 4>(split_v, grid, st, args);
+hipError_t launch_d(int groups, bool split_v, dim3 grid, hipStream_t st,
+                    const DecodeArgs& args) {
+  switch (groups) {
+    case 1: return launch_g<D, 1>(split_v, grid, st, args);
+    case 2: return launch_g<D, 2>(split_v, grid, st, args);
+    default: return launch_g<D, 4>(split_v, grid, st, args);
   }
 }
 
-template <int D>
-hipError_t launch_combine_d(int R, hipStream_t st, CombineArgs args) {
-  constexpr int kHPB = 256 / (D / 8);
-  args.head_groups = (args.H + kHPB - 1) / kHPB;
-  hipLaunchKernelGGL((dsa_combine_kernel<D>), dim3(R * args.head_groups), dim3(256), 0, st, args);
-  return hipGetLastError();
-}
-
-// Token-split factor of a head block: how many waves share one 16-head group.
-int token_split(int heads_in_block) {
+// 16-head groups a workgroup runs for a head block of this many heads.
+int head_groups(int heads_in_block) {
   const int groups = (heads_in_block + 15) / 16;
-  if (groups >= 3) return 1;
-  if (groups == 2) return 2;
-  return 4;
+  return groups >= 3 ? 4 : groups;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_workspace(dsa_decode_plan_t plan, const void* workspace, size_t workspace_bytes,
+                    const char* who) {
+  if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < plan->ws.total) {
+    std::ostringstream m;
+    m << who << ": workspace " << workspace << " of " << workspace_bytes << " bytes; need "
+      << plan->ws.total << " bytes, 256-byte aligned";
+    return fail(DSA_DECODE_ERR_WORKSPACE, m.str());
+  }
+  return DSA_DECODE_OK;
+}
+
+int check_device(dsa_decode_plan_t plan, const char* who) {
+  if (plan->device < 0) {
+    std::ostringstream m;
+    m << who << ": host-only plan (device -1) cannot launch";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != plan->device) {
+    std::ostringstream m;
+    m << who << ": current HIP device is " << cur << ", plan was made for " << plan->device;
+    return fail(DSA_DECODE_ERR_DEVICE, m.str());
+  }
+  return DSA_DECODE_OK;
+}
 
 }  // namespace
 }  // namespace dsa
@@ -759,6 +865,25 @@ void dsa_decode_plan_destroy(dsa_decode_plan_t plan) {
   delete plan;
 }
 
+int dsa_decode_workspace_init(dsa_decode_plan_t plan, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  using namespace dsa;
+  if (!plan) return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_workspace_init: plan is NULL");
+  int st = check_device(plan, "dsa_decode_workspace_init");
+  if (st != DSA_DECODE_OK) return st;
+  st = check_workspace(plan, workspace, workspace_bytes, "dsa_decode_workspace_init");
+  if (st != DSA_DECODE_OK) return st;
+  const size_t words = plan->ws.total / sizeof(int32_t);
+  const int blocks = (int)std::min<size_t>((words + 255) / 256, 1024);
+  hipLaunchKernelGGL(dsa_zero_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     (int32_t*)workspace, words);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(DSA_DECODE_ERR_LAUNCH,
+                std::string("dsa_decode_workspace_init: ") + hipGetErrorString(e));
+  return DSA_DECODE_OK;
+}
+
 int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables,
                       const int32_t* seq_lens, const int32_t* sel_indices,
@@ -766,112 +891,71 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
                       size_t workspace_bytes, void* stream) {
   using namespace dsa;
   if (!plan) return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_launch: plan is NULL");
-  if (plan->device < 0)
-    return fail(DSA_DECODE_ERR_INVALID,
-                "dsa_decode_launch: host-only plan (device -1) cannot launch");
+  int st = check_device(plan, "dsa_decode_launch");
+  if (st != DSA_DECODE_OK) return st;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !sel_indices || !out)
     return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_launch: NULL device pointer");
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(DSA_DECODE_ERR_INVALID,
                 "dsa_decode_launch: q, out, k_cache and v_cache must be 16-byte aligned");
-  if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
-    return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_launch: k_scale and v_scale must be finite");
-  if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < plan->ws.total) {
+  if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale)) {
     std::ostringstream m;
-    m << "dsa_decode_launch: workspace " << workspace << " of " << workspace_bytes
-      << " bytes; need " << plan->ws.total << " bytes, 256-byte aligned";
-    return fail(DSA_DECODE_ERR_WORKSPACE, m.str());
+    m << "dsa_decode_launch: k_scale must be finite and > 0 and v_scale finite (got "
+      << k_scale << ", " << v_scale << ")";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess || cur != plan->device) {
-    std::ostringstream m;
-    m << "dsa_decode_launch: current HIP device is " << cur << ", plan was made for "
-      << plan->device;
-    return fail(DSA_DECODE_ERR_DEVICE, m.str());
-  }
+  st = check_workspace(plan, workspace, workspace_bytes, "dsa_decode_launch");
+  if (st != DSA_DECODE_OK) return st;
 
   const dsa_decode_params& p = plan->p;
-  hipStream_t st = (hipStream_t)stream;
+  const hipStream_t stream_h = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
-  int32_t* ids = (int32_t*)(ws + plan->ws.ids);
-  uint64_t* offs = (uint64_t*)(ws + plan->ws.offsets);
-  int32_t* counts = (int32_t*)(ws + plan->ws.counts);
 
   hipEvent_t* ev = nullptr;
   if (plan->timing_count < plan->timing_capacity)
-    ev = (hipEvent_t*)&plan->events[4 * plan->timing_count++];
-  if (ev) (void)hipEventRecord(ev[0], st);
+    ev = (hipEvent_t*)&plan->events[2 * plan->timing_count++];
+  if (ev) (void)hipEventRecord(ev[0], stream_h);
 
-  SelectArgs sa;
-  sa.sel = sel_indices;
-  sa.seq_lens = seq_lens;
-  sa.block_tables = block_tables;
-  sa.ids = ids;
-  sa.offsets = offs;
-  sa.counts = counts;
-  sa.cache_stride = p.cache_stride_bytes;
-  sa.width = p.sel_width;
-  sa.max_seq_len = p.max_seq_len;
-  sa.bt_stride = p.block_table_stride;
-  sa.block_size = p.block_size;
-  sa.D = p.kv_lora_rank;
-  hipLaunchKernelGGL(dsa_select_kernel, dim3(p.num_rows), dim3(kSelThreads), 0, st, sa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess)
-    return fail(DSA_DECODE_ERR_LAUNCH,
-                std::string("dsa_decode_launch: selection kernel: ") + hipGetErrorString(e));
-  if (ev) (void)hipEventRecord(ev[1], st);
-
-  AttendArgs aa;
-  aa.q = (const uint16_t*)q;
-  aa.k_cache = (const uint8_t*)k_cache;
-  aa.v_cache = (const uint8_t*)v_cache;
-  aa.counts = counts;
-  aa.offsets = offs;
-  aa.out = (uint16_t*)out;
-  aa.part_o = plan->chunks > 1 ? (float*)(ws + plan->ws.part_o) : nullptr;
-  aa.part_ml = plan->chunks > 1 ? (float*)(ws + plan->ws.part_ml) : nullptr;
-  aa.H = p.num_q_heads;
-  aa.width = p.sel_width;
-  aa.chunks = plan->chunks;
-  aa.chunk_tokens = plan->chunk_tokens;
-  aa.head_blocks = plan->head_blocks;
-  aa.scale_log2 = p.sm_scale * k_scale * kLog2e;
-  aa.v_scale = v_scale;
-  const int ts = token_split(p.num_q_heads < kHeadsPerBlock ? p.num_q_heads : kHeadsPerBlock);
+  DecodeArgs da;
+  da.q = (const uint16_t*)q;
+  da.k_cache = (const uint8_t*)k_cache;
+  da.v_cache = (const uint8_t*)v_cache;
+  da.block_tables = block_tables;
+  da.seq_lens = seq_lens;
+  da.sel = sel_indices;
+  da.out = (uint16_t*)out;
+  da.ws_ids = (int32_t*)(ws + plan->ws.ids);
+  da.ws_offsets = (uint64_t*)(ws + plan->ws.offsets);
+  da.ws_counts = (int32_t*)(ws + plan->ws.counts);
+  da.ws_arrivals = (int32_t*)(ws + plan->ws.arrivals);
+  da.part_o = plan->chunks > 1 ? (float*)(ws + plan->ws.part_o) : nullptr;
+  da.part_ml = plan->chunks > 1 ? (float*)(ws + plan->ws.part_ml) : nullptr;
+  da.stride_rows = (uint32_t)(p.cache_stride_bytes / (uint64_t)p.kv_lora_rank);
+  da.H = p.num_q_heads;
+  da.width = p.sel_width;
+  da.max_seq_len = p.max_seq_len;
+  da.bt_stride = p.block_table_stride;
+  da.block_size = p.block_size;
+  da.chunks = plan->chunks;
+  da.chunk_tokens = plan->chunk_tokens;
+  da.head_blocks = plan->head_blocks;
+  da.scale_log2 = p.sm_scale * k_scale * kLog2e;
+  da.v_scale = v_scale;
+  const int groups =
+      head_groups(p.num_q_heads < kHeadsPerBlock ? p.num_q_heads : kHeadsPerBlock);
   const bool split_v = k_cache != v_cache;
   const dim3 grid(p.num_rows * plan->head_blocks * plan->chunks);
+  hipError_t e;
   switch (p.kv_lora_rank) {
-    case 64: e = launch_attend_d<64>(ts, split_v, grid, st, aa); break;
-    case 128: e = launch_attend_d<128>(ts, split_v, grid, st, aa); break;
-    case 256: e = launch_attend_d<256>(ts, split_v, grid, st, aa); break;
-    default: e = launch_attend_d<512>(ts, split_v, grid, st, aa); break;
+    case 64: e = launch_d<64>(groups, split_v, grid, stream_h, da); break;
+    case 128: e = launch_d<128>(groups, split_v, grid, stream_h, da); break;
+    case 256: e = launch_d<256>(groups, split_v, grid, stream_h, da); break;
+    default: e = launch_d<512>(groups, split_v, grid, stream_h, da); break;
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,
-                std::string("dsa_decode_launch: attend kernel: ") + hipGetErrorString(e));
-  if (ev) (void)hipEventRecord(ev[2], st);
-
-  if (plan->chunks > 1) {
-    CombineArgs ca;
-    ca.part_o = aa.part_o;
-    ca.part_ml = aa.part_ml;
-    ca.out = (uint16_t*)out;
-    ca.H = p.num_q_heads;
-    ca.chunks = plan->chunks;
-    ca.head_groups = 0;
-    ca.v_scale = v_scale;
-    switch (p.kv_lora_rank) {
-      case 64: e = launch_combine_d<64>(p.num_rows, st, ca); break;
-      case 128: e = launch_combine_d<128>(p.num_rows, st, ca); break;
-      case 256: e = launch_combine_d<256>(p.num_rows, st, ca); break;
-      default: e = launch_combine_d<512>(p.num_rows, st, ca); break;
-    }
-    if (e != hipSuccess)
-      return fail(DSA_DECODE_ERR_LAUNCH,
-                  std::string("dsa_decode_launch: combine kernel: ") + hipGetErrorString(e));
-  }
-  if (ev) (void)hipEventRecord(ev[3], st);
+                std::string("dsa_decode_launch: decode kernel: ") + hipGetErrorString(e));
+  if (ev) (void)hipEventRecord(ev[1], stream_h);
   return DSA_DECODE_OK;
 }
 
@@ -881,22 +965,22 @@ int dsa_decode_read_selection(dsa_decode_plan_t plan, const void* workspace,
   using namespace dsa;
   if (!plan || !workspace)
     return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_read_selection: NULL plan or workspace");
-  if (plan->device < 0)
-    return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_read_selection: host-only plan");
+  int st = check_device(plan, "dsa_decode_read_selection");
+  if (st != DSA_DECODE_OK) return st;
   if (workspace_bytes < plan->ws.total)
     return fail(DSA_DECODE_ERR_WORKSPACE, "dsa_decode_read_selection: workspace too small");
   const uint8_t* ws = (const uint8_t*)workspace;
   const size_t RW = (size_t)plan->p.num_rows * plan->p.sel_width;
-  hipStream_t st = (hipStream_t)stream;
+  const hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (ids && e == hipSuccess)
-    e = hipMemcpyAsync(ids, ws + plan->ws.ids, RW * sizeof(int32_t), hipMemcpyDeviceToDevice, st);
+    e = hipMemcpyAsync(ids, ws + plan->ws.ids, RW * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
   if (counts && e == hipSuccess)
     e = hipMemcpyAsync(counts, ws + plan->ws.counts, plan->p.num_rows * sizeof(int32_t),
-                       hipMemcpyDeviceToDevice, st);
+                       hipMemcpyDeviceToDevice, s);
   if (offsets && e == hipSuccess)
     e = hipMemcpyAsync(offsets, ws + plan->ws.offsets, RW * sizeof(uint64_t),
-                       hipMemcpyDeviceToDevice, st);
+                       hipMemcpyDeviceToDevice, s);
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,
                 std::string("dsa_decode_read_selection: ") + hipGetErrorString(e));
@@ -909,7 +993,7 @@ int dsa_decode_timing_begin(dsa_decode_plan_t plan, int32_t max_launches) {
     return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_timing_begin: bad plan or count");
   for (void* e : plan->events)
     if (e) (void)hipEventDestroy((hipEvent_t)e);
-  plan->events.assign((size_t)4 * max_launches, nullptr);
+  plan->events.assign((size_t)2 * max_launches, nullptr);
   for (auto& e : plan->events) {
     hipEvent_t h;
     if (hipEventCreate(&h) != hipSuccess)
@@ -925,19 +1009,17 @@ int dsa_decode_timing_end(dsa_decode_plan_t plan, float* kernel_ms, int32_t* lau
   using namespace dsa;
   if (!plan || !kernel_ms || !launches)
     return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_timing_end: NULL argument");
-  kernel_ms[0] = kernel_ms[1] = kernel_ms[2] = 0.f;
+  *kernel_ms = 0.f;
   *launches = plan->timing_count;
   int status = DSA_DECODE_OK;
   for (int i = 0; i < plan->timing_count; ++i) {
-    hipEvent_t* ev = (hipEvent_t*)&plan->events[4 * i];
-    if (hipEventSynchronize(ev[3]) != hipSuccess) {
+    hipEvent_t* ev = (hipEvent_t*)&plan->events[2 * i];
+    if (hipEventSynchronize(ev[1]) != hipSuccess) {
       status = fail(DSA_DECODE_ERR_DEVICE, "dsa_decode_timing_end: hipEventSynchronize failed");
       break;
     }
-    for (int k = 0; k < 3; ++k) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, ev[k], ev[k + 1]) == hipSuccess) kernel_ms[k] += ms;
-    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess) *kernel_ms += ms;
   }
   for (void* e : plan->events)
     if (e) (void)hipEventDestroy((hipEvent_t)e);

@@ -91,9 +91,16 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
       << " is smaller than one page (block_size * kv_lora_rank = " << row_bytes << ")";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  if (stride % 16 != 0) {
+  // Latent rows are addressed by index (byte offset / kv_lora_rank), so a
+  // page must start on a row boundary.
+  if (stride % (uint64_t)p->kv_lora_rank != 0) {
     m << "dsa_decode_plan: cache_stride_bytes " << stride
-      << " is not a multiple of 16";
+      << " is not a multiple of kv_lora_rank " << p->kv_lora_rank;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (stride / (uint64_t)p->kv_lora_rank > UINT32_MAX) {
+    m << "dsa_decode_plan: cache_stride_bytes " << stride
+      << " spans more than 2^32 latent rows";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
   // A per-row table must cover every position the row may attend: its entry
@@ -166,11 +173,16 @@ void plan_layout(dsa_decode_plan_s* plan) {
   off = align_up(off + sizeof(uint64_t) * R * W, kWsAlign);
   L.counts = off;
   off = align_up(off + sizeof(int32_t) * R, kWsAlign);
+  L.arrivals = off;
+  off = align_up(off + sizeof(int32_t) * R * plan->head_blocks, kWsAlign);
   if (plan->chunks > 1) {
+    // Partials are kept per workgroup for a full block of kHeadsPerBlock
+    // heads (a block that holds fewer heads still stores whole head groups).
+    const int64_t slots = R * plan->head_blocks * plan->chunks * kHeadsPerBlock;
     L.part_o = off;
-    off = align_up(off + sizeof(float) * R * plan->chunks * H * D, kWsAlign);
+    off = align_up(off + sizeof(float) * slots * D, kWsAlign);
     L.part_ml = off;
-    off = align_up(off + sizeof(float) * R * plan->chunks * H * 2, kWsAlign);
+    off = align_up(off + sizeof(float) * slots * 2, kWsAlign);
   }
   L.total = off;
 }
@@ -243,8 +255,8 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->chunk_tokens = plan->chunk_tokens;
   info->chunks_per_row = plan->chunks;
   info->head_blocks = plan->head_blocks;
-  info->attend_workgroups = plan->p.num_rows * plan->head_blocks * plan->chunks;
-  info->uses_combine = plan->chunks > 1 ? 1 : 0;
+  info->workgroups = plan->p.num_rows * plan->head_blocks * plan->chunks;
+  info->merges_chunks = plan->chunks > 1 ? 1 : 0;
   info->num_cus = plan->num_cus;
   info->reserved = 0;
   info->workspace_bytes = plan->ws.total;

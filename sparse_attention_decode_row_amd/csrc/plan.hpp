@@ -11,12 +11,12 @@
 
 namespace dsa {
 
-// Granularity of a chunk (the selected tokens one attend workgroup takes).
+// Granularity of a chunk (the selected tokens one workgroup takes).
 constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
-// Largest chunk one attend workgroup handles (its byte-offset table lives in
-// LDS: 2048 x 8 B = 16 KiB).
+// Largest chunk one workgroup handles (its latent-row table lives in LDS:
+// 2048 x 4 B = 8 KiB).
 constexpr int kMaxChunkTokens = 2048;
-// Heads one attend workgroup covers (4 waves x 16 heads).
+// Heads one workgroup covers (4 groups of 16 heads, two waves per group).
 constexpr int kHeadsPerBlock = 64;
 // Workspace sub-buffer alignment.
 constexpr size_t kWsAlign = 256;
@@ -25,8 +25,9 @@ struct WorkspaceLayout {
   size_t ids = 0;       // int32 [R, W]
   size_t offsets = 0;   // uint64 [R, W]
   size_t counts = 0;    // int32 [R]
-  size_t part_o = 0;    // float [R, C, H, D]   (C > 1 only)
-  size_t part_ml = 0;   // float [R, C, H, 2]   (C > 1 only)
+  size_t arrivals = 0;  // int32 [R, head_blocks] (zero between launches)
+  size_t part_o = 0;    // float [R, head_blocks, C, 64 heads, D] (C > 1 only)
+  size_t part_ml = 0;   // float [R, head_blocks, C, 64 heads, 2] (C > 1 only)
   size_t total = 0;
 };
 
@@ -41,7 +42,7 @@ struct dsa_decode_plan_s {
   int head_blocks = 1;
   dsa::WorkspaceLayout ws;
   // benchmark timing (dsa_decode_timing_begin / _end)
-  std::vector<void*> events;      // hipEvent_t, 4 per recorded launch
+  std::vector<void*> events;      // hipEvent_t, 2 per recorded launch
   int timing_capacity = 0;
   int timing_count = 0;
 };

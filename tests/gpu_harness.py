@@ -64,7 +64,7 @@ def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
     s = i32(sl_)
     out = torch.full_like(q, float("nan"))
     plan = plan_for(wl, chunk_tokens, max_seq_len=max_seq_len)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev())
+    ws = plan.new_workspace()
     plan.launch(q, k_pool, v_pool, bt, sl, s, wl.k_scale, wl.v_scale, out, ws)
     ids = counts = offs = None
     if with_selection:

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(native):
 
 
 def test_version(native):
-    assert native.lib().dsa_decode_version() == 100
+    assert native.lib().dsa_decode_version() == 200
 
 
 def plan(native, **kw):
@@ -63,7 +63,8 @@ def plan(native, **kw):
     (dict(max_seq_len=0), -1, "max_seq_len must be > 0"),
     (dict(block_table_stride=-1), -1, "block_table_stride must be >= 0"),
     (dict(cache_stride_bytes=1000), -1, "smaller than one page"),
-    (dict(cache_stride_bytes=64 * 512 + 8), -1, "not a multiple of 16"),
+    (dict(cache_stride_bytes=64 * 512 + 8), -1, "not a multiple of kv_lora_rank"),
+    (dict(cache_stride_bytes=64 * 512 + 256), -1, "not a multiple of kv_lora_rank"),
     (dict(block_table_stride=100), -1, "block-table entries per row"),
     (dict(sm_scale=float("inf")), -1, "sm_scale must be finite"),
     (dict(chunk_tokens=100), -1, "chunk_tokens"),
@@ -117,18 +118,19 @@ def test_split_plan(native, kw, chunks, ct):
     info = plan(native, **kw).info()
     assert info["chunks_per_row"] == chunks
     assert info["chunk_tokens"] == ct
-    assert info["uses_combine"] == (chunks > 1)
+    assert info["merges_chunks"] == (chunks > 1)
+    assert info["workgroups"] == info["chunks_per_row"] * info["head_blocks"] * (kw.get("num_rows", 128))
     assert info["device"] == -1
 
 
 def test_workspace_layout(native):
     p = plan(native)
     R, W, C, H, D = 128, 2048, 2, 64, 512
-    need = R * W * 4 + R * W * 8 + R * 4 + R * C * H * D * 4 + R * C * H * 2 * 4
-    assert need <= p.workspace_bytes <= need + 5 * 256
+    need = R * W * 4 + R * W * 8 + R * 4 + R * 4 + R * C * H * D * 4 + R * C * H * 2 * 4
+    assert need <= p.workspace_bytes <= need + 6 * 256
     p1 = plan(native, num_rows=256, max_seq_len=32768, block_table_stride=512)
     assert p1.info()["chunks_per_row"] == 1
-    assert p1.workspace_bytes <= 256 * 2048 * 12 + 256 * 4 + 3 * 256
+    assert p1.workspace_bytes <= 256 * 2048 * 12 + 256 * 8 + 4 * 256
 
 
 def test_head_blocks(native):

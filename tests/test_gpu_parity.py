@@ -118,6 +118,9 @@ CASES = [
     (7, 2, 64, 512, 64, 1000, 900, 256, True, True),
     (8, 4, 1, 512, 8, 150, 64, 0, False, False),
     (9, 3, 128, 256, 64, 2600, 2500, 1024, False, False),
+    (10, 3, 64, 64, 16, 1200, 900, 64, False, False),
+    (11, 2, 40, 256, 32, 3000, 2000, 0, False, True),
+    (12, 2, 96, 128, 32, 1500, 1400, 128, True, False),
 ]
 
 
@@ -331,6 +334,7 @@ def test_launch_rejects_bad_arguments(H):
     bt, sl, sel = H.i32(wl.block_tables), H.i32(wl.seq_lens), H.i32(wl.sel)
     out = torch.empty_like(q)
     ws = torch.empty(plan.workspace_bytes + 512, dtype=torch.uint8, device=q.device)
+    plan.workspace_init(ws)
     with pytest.raises(dsa.DsaDecodeError) as e:
         plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws,
                     workspace_bytes=plan.workspace_bytes - 1)
