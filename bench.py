@@ -193,9 +193,32 @@ def main():
                  "fp8_issued_flops_per_launch": 2 * flops, "fp8_peak": 5000.0},
     }
 
+    measured = measured_traffic(name)
+    if measured is not None:
+        result["roofline"]["traffic"] = measured
+        result["roofline"]["traffic_unit"] = ("bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE "
+                                              "scaled by a 256 MiB copy's readings")
     if args.cpu_rows > 0:
         result["cpu_baseline"] = cpu_baseline(base, pool, batches[0], args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary of this
+    workload, or None when there is none or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"dsa_decode_kernel_{workload}_hbm_counters.json")
+    src = os.path.join(ROOT, "sparse_attention_decode_row_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, pool_dev, batch, nrows):
