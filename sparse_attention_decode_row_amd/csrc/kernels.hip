@@ -78,6 +78,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// One 16-byte-per-lane DMA from global memory into LDS: lane l's 16 bytes
+// land at l_base + 16*l. Issued as inline assembly on purpose: the
+// compiler's wait-count pass cannot tell when such a transfer completes, and
+// with the builtin in a loop it falls back to waiting for every outstanding
+// LDS read at each use, which defeats operand prefetching. Completion is
+// ordered explicitly here: wait_vmcnt<0>() and a barrier before the tile is
+// read. M0 needs one wait state after it is written.
+__device__ __forceinline__ void dma16(const void* g, DSA_LDS void* l_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(m0v) : "memory", "m0");
+}
+
 // Workgroup barrier that does not wait for outstanding global/DMA loads
 // (a plain __syncthreads would drain the prefetch pipeline). LDS reads and
 // writes issued before it are complete once every wave arrives.
@@ -128,14 +141,21 @@ __device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Device-coherent (agent-scope) scalar store / load: written through to, and
-// read from, the level shared by all XCDs, so the split partials leave no
-// dirty L2 lines for the release fence to write back.
+// Device-coherent (agent-scope) scalar store: written through to the level
+// shared by all XCDs, so the split partials leave no dirty L2 lines for the
+// release fence to write back.
 __device__ __forceinline__ void store_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// 16-byte device-coherent store (written through to the level all XCDs
+// share). Inline assembly: the compiler does not track its completion, so
+// the caller waits with wait_vmcnt<0>() before publishing the data; nor does
+// it see the store-data hazard (a store of more than 8 bytes reads its data
+// registers after issue), so the wait states that let the next instruction
+// overwrite them are inside the statement.
+__device__ __forceinline__ void store_dev16(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 // Max / sum over lane pairs 16 (resp. 32) apart through the cross-row lane
@@ -177,29 +197,17 @@ __device__ __forceinline__ int tile_swizzle(int slot) {
   return ((slot & 15) ^ ((slot & 16) >> 1)) & kMask;
 }
 
-// Exclusive prefix sum of one value per thread over the workgroup; *total
-// receives the sum over all threads.
-template <int kWaves>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) sh[w] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    const int s = sh[k];
-    all += s;
-    if (k < w) before += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts
+// (within rows of 16 lanes) and row broadcasts (across rows); lanes a shift
+// leaves without a source, and rows a broadcast does not target, add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
 }
 
 struct DecodeArgs {
@@ -213,7 +221,7 @@ struct DecodeArgs {
   int32_t* ws_ids;       // [R, W] distinct ids, ascending (exported)
   uint64_t* ws_offsets;  // [R, W] their latent-row byte offsets (exported)
   int32_t* ws_counts;    // [R]
-  int32_t* ws_arrivals;  // [R * head_blocks] chunks finished; the merger resets it
+  int32_t* ws_arrivals;  // [2][R * head_blocks] chunks arrived / partials published; reset by the merger
   float* part_o;         // [R, C, H, D]
   float* part_ml;        // [R, C, H, 2]
   uint32_t stride_rows;  // cache_stride_bytes / D
@@ -225,6 +233,7 @@ struct DecodeArgs {
   int chunks;
   int chunk_tokens;
   int head_blocks;
+  int rows_hb;       // R * head_blocks (stride between the two counter arrays)
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
 };
@@ -292,73 +301,109 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
   // ascending rank cstart .. cend - 1.
   const int cstart = c * a.chunk_tokens, cend = cstart + a.chunk_tokens;
   const int32_t* srow = a.sel + (size_t)r * a.width;
-  // Loads in the order they are waited for (the counter drains in issue
-  // order): the length, a selection row of up to 4 ids per thread, then the
-  // query slice of this lane (head li, latent columns 128*ks + 32*g +
-  // [0, 32)), which is only needed after the selection.
+  // The length and up to 4 ids per thread are loaded first, from addresses
+  // clamped into their buffers (no branches); the query is loaded only once
+  // the ids are in, so that its traffic does not delay them.
   int L = a.seq_lens[r];
-  const bool ids_in_regs = a.width <= 4 * kThreads;
-  int tpre[4];
+  int tpre[4];  // ids tid + u*kThreads (u < 4); the rest of a wider row is loaded per window
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = tid + u * kThreads;
-    tpre[u] = ids_in_regs && j < a.width ? srow[j] : -1;
-  }
-  u32x4 qraw[kKSteps][4];
-  {
+  for (int u = 0; u < 4; ++u) tpre[u] = srow[min(tid + u * kThreads, a.width - 1)];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (tid + u * kThreads >= a.width) tpre[u] = -1;
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+
+  // This wave's share of the query: head li, latent columns 128*ks + 32*g +
+  // [0, 32). With several k-steps a wave takes ks = 2*i + hf, the other wave
+  // of the group converts the rest and the two exchange the FP8 terms
+  // through the second tile buffer (4 KiB per group and k-step: exactly one
+  // buffer at four groups); a single k-step is loaded by both waves.
+  constexpr bool kShareQ = kKSteps >= 2;
+  constexpr int kKOwn = kShareQ ? (kKSteps + 1) / 2 : kKSteps;
+  static_assert(!kShareQ || kGroups * kKSteps * 4096 <= kTileBytes, "query exchange area");
+  auto own_ks = [&](int i) { return kShareQ ? 2 * i + hf : i; };
+  u32x4 qraw[kKOwn][4];
+  auto load_q = [&]() {
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (head_ok ? head : 0)) * D;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const int d0 = 128 * ks + 32 * g;
-      const bool ok = head_ok && d0 < D;
+    for (int i = 0; i < kKOwn; ++i) {
+      const int ks = min(own_ks(i), kKSteps - 1);
+      const int d0 = min(128 * ks + 32 * g, D - 32);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        qraw[ks][v] = ok ? *(const u32x4*)(qrow + d0 + 8 * v) : u32x4{0u, 0u, 0u, 0u};
+      for (int v = 0; v < 4; ++v) qraw[i][v] = *(const u32x4*)(qrow + d0 + 8 * v);
     }
-  }
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  };
+
   uint32_t* bitmap = (uint32_t*)smem;
+  const DSA_LDS u32x4* bitmap4 = (const DSA_LDS u32x4*)smem;
   if (tid == 0) flag_sh = 0;
   int total = 0;
+  bool q_loaded = false;
   for (int base = 0; base < L; base += kBitmapWords * 32) {
     const int span = min(kBitmapWords * 32, L - base);
     const int nwords = (span + 31) >> 5;
-    for (int i = tid; i < nwords; i += kThreads) bitmap[i] = 0u;
+    const int per = ((nwords + kThreads - 1) / kThreads + 3) & ~3;  // words per thread
+    for (int i = tid; i < per * kThreads / 4; i += kThreads)
+      ((u32x4*)bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // a hole (any negative id) or an id outside [0, L) sets nothing
-    for (int j0 = tid; j0 < a.width; j0 += 4 * kThreads) {
-      int t[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + u * kThreads;
-        t[u] = ids_in_regs ? tpre[u] : (j < a.width ? srow[j] : -1);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (t[u] >= base && t[u] - base < span)
-          atomicOr(&bitmap[(t[u] - base) >> 5], 1u << ((t[u] - base) & 31));
+    for (int u = 0; u < 4; ++u)
+      if (tpre[u] >= base && tpre[u] - base < span)
+        atomicOr(&bitmap[(tpre[u] - base) >> 5], 1u << ((tpre[u] - base) & 31));
+    for (int j = tid + 4 * kThreads; j < a.width; j += kThreads) {
+      const int t = srow[j];
+      if (t >= base && t - base < span)
+        atomicOr(&bitmap[(t - base) >> 5], 1u << ((t - base) & 31));
+    }
+    if (!q_loaded) {
+      load_q();
+      q_loaded = true;
     }
     __syncthreads();
-    const int per = (nwords + kThreads - 1) / kThreads;
-    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
+    // rank of this thread's first word: wave scan, then the waves before it
+    const int w0 = tid * per;
     int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
-    int blk_total;
-    int rank = total + block_exclusive_scan<kWaves>(cnt, scan_sh, &blk_total);
+    for (int w = w0; w < w0 + per; w += 4) {
+      const u32x4 x = bitmap4[w >> 2];
+      cnt += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
+    }
+    const int incl = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) scan_sh[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+      const int sw = scan_sh[k];
+      all += sw;
+      before += k < wave ? sw : 0;
+    }
+    int rank = total + before + incl - cnt;
     if (rank < cend && rank + cnt > cstart) {
-      for (int w = w0; w < w1 && rank < cend; ++w) {
-        uint32_t bits = bitmap[w];
-        while (bits && rank < cend) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          if (rank >= cstart) rows_lds[rank - cstart] = (uint32_t)(base + (w << 5) + b);
-          ++rank;
+      for (int w = w0; w < w0 + per && rank < cend; w += 4) {
+        const u32x4 x = bitmap4[w >> 2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t bits = x[e];
+          const int pc = __popc(bits);
+          if (rank + pc > cstart && rank < cend) {
+            while (bits) {
+              const int b = __ffs(bits) - 1;
+              bits &= bits - 1;
+              if (rank >= cstart && rank < cend)
+                rows_lds[rank - cstart] = (uint32_t)(base + ((w + e) << 5) + b);
+              ++rank;
+            }
+          } else {
+            rank += pc;
+          }
         }
       }
     }
-    total += blk_total;
-    __syncthreads();
+    total += all;
+    __syncthreads();  // the bitmap and scan_sh are reused by the next window
   }
+  if (!q_loaded) load_q();
   const int n = max(0, min(a.chunk_tokens, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
 
@@ -377,8 +422,10 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       for (int u = 0; u < 4; ++u)
         t[u] = i0 + u * kThreads < n ? (int)rows_lds[i0 + u * kThreads] : 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        t[u] = min(max(t[u], 0), L - 1);  // a no-op for every id the bitmap produced
         page[u] = i0 + u * kThreads < n ? (uint32_t)bt[t[u] / a.block_size] : 0u;
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * kThreads;
@@ -393,12 +440,70 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       }
     }
     if (c == 0 && hb == 0 && tid == 0) a.ws_counts[r] = total;
-    __syncthreads();
-    // pad to whole tiles with the last real row (loaded, weighted by zero)
-    if (n > 0)
-      for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
-    __syncthreads();
   }
+
+  // ---- the query as two FP8 terms under a per-head power-of-two scale that
+  // puts the head's largest |q| in [128, 256)
+  i32x8 qhi[kKSteps], qlo[kKSteps];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kKOwn; ++i) {
+    const int ks = own_ks(i);
+    if (!head_ok || ks >= kKSteps || 128 * ks + 32 * g >= D)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) qraw[i][v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[i][v][e])), fabsf(bf16_hi(qraw[i][v][e]))));
+  }
+  amax = max_xor32(max_xor16(amax));
+  if constexpr (kShareQ) xch_f[wave][lane] = amax;
+  __syncthreads();  // row table written; both halves' maxima visible
+  // pad to whole tiles with the last real row (loaded, weighted by zero)
+  if (n > 0)
+    for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
+  float score_scale;
+  {
+    if constexpr (kShareQ) amax = fmaxf(amax, xch_f[mate][lane]);
+    const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
+    int sh = 7 - e;
+    sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+    const float qs = pow2i(sh);
+    u32x4* qx = (u32x4*)(smem + kTileBytes);  // [group][ks][hi|lo][half][lane]
+#pragma unroll
+    for (int i = 0; i < kKOwn; ++i) {
+      const int ks = own_ks(i);
+      if (ks >= kKSteps) continue;
+      u32x4 h[2], l[2];
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const unsigned w0 = qraw[i][v][2 * h2], w1 = qraw[i][v][2 * h2 + 1];
+          int hi, lo;
+          split_fp8x4(bf16_lo(w0) * qs, bf16_hi(w0) * qs, bf16_lo(w1) * qs, bf16_hi(w1) * qs,
+                      hi, lo);
+          h[v >> 1][2 * (v & 1) + h2] = (unsigned)hi;
+          l[v >> 1][2 * (v & 1) + h2] = (unsigned)lo;
+        }
+      if constexpr (kShareQ) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + half) * kWave + lane] = h[half];
+          qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + half) * kWave + lane] = l[half];
+        }
+      } else {
+        qhi[ks] = i32x8{(int)h[0].x, (int)h[0].y, (int)h[0].z, (int)h[0].w,
+                        (int)h[1].x, (int)h[1].y, (int)h[1].z, (int)h[1].w};
+        qlo[ks] = i32x8{(int)l[0].x, (int)l[0].y, (int)l[0].z, (int)l[0].w,
+                        (int)l[1].x, (int)l[1].y, (int)l[1].z, (int)l[1].w};
+      }
+    }
+    score_scale = a.scale_log2 * pow2i(-sh);
+  }
+  __syncthreads();  // row table padded; both halves' FP8 terms visible
 
   // -------------------------------------------------------------- 2. gather
   // Wave w moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its instruction k
@@ -418,8 +523,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       const int slot0 = wave * kTPW + k * kTokPerInstr;
       const int swz = tile_swizzle<D>(slot0 + j);
       const uint64_t off = (uint64_t)row[k] * (uint64_t)D + (uint64_t)((ci ^ swz) << 4);
-      __builtin_amdgcn_global_load_lds(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D),
-                                       16, 0, 0);
+      dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
     }
   };
   // Token index (within the tile) held by LDS slot s.
@@ -427,44 +531,22 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
     const int w = s / kTPW, sw = s % kTPW;
     return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
   };
-  if (ntiles > 0) {
-    issue_tile(0, 0, a.k_cache);
-    if constexpr (kSplitV) issue_tile(0, kTileBytes, a.v_cache);
-  }
+  // Tile 0's K (and, when K and V are the same bytes, its V) goes out now;
+  // a separate V buffer is filled at the top of the first tile, after every
+  // wave has read its query terms out of it.
+  if (ntiles > 0) issue_tile(0, 0, a.k_cache);
 
-  // ---- the query slice as two FP8 terms under a per-head power-of-two
-  // scale that puts the head's largest |q| in [128, 256)
-  i32x8 qhi[kKSteps], qlo[kKSteps];
-  float score_scale;
-  {
-    const auto& raw = qraw;
-    float amax = 0.f;
+  if constexpr (kShareQ) {
+    const u32x4* qx = (const u32x4*)(smem + kTileBytes);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(raw[ks][v][e])), fabsf(bf16_hi(raw[ks][v][e]))));
-    amax = max_xor32(max_xor16(amax));
-    const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
-    int sh = 7 - e;
-    sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
-    const float qs = pow2i(sh);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const unsigned w0 = raw[ks][v][2 * h2], w1 = raw[ks][v][2 * h2 + 1];
-          int hi, lo;
-          split_fp8x4(bf16_lo(w0) * qs, bf16_hi(w0) * qs, bf16_lo(w1) * qs, bf16_hi(w1) * qs,
-                      hi, lo);
-          qhi[ks][2 * v + h2] = hi;
-          qlo[ks][2 * v + h2] = lo;
-        }
-    score_scale = a.scale_log2 * pow2i(-sh);
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
+      const u32x4 h1 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 1) * kWave + lane];
+      const u32x4 l0 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 0) * kWave + lane];
+      const u32x4 l1 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 1) * kWave + lane];
+      qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+      qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+    }
   }
 
   // K operand addresses. This wave scores blocks b = 4*hf + k (k < 4) of 16
@@ -511,10 +593,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
     bool overflow = false;
-    if (pass == 1 && ntiles > 0) {
-      issue_tile(0, 0, a.k_cache);
-      if constexpr (kSplitV) issue_tile(0, kTileBytes, a.v_cache);
-    }
+    if (pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
 
     for (int it = 0; it < ntiles; ++it) {
       wait_vmcnt<0>();
@@ -523,14 +602,14 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       if constexpr (kSplitV) {
         koff = 0;
         voff = kTileBytes;
-        if (it > 0) issue_tile(it, kTileBytes, a.v_cache);  // V buffer is free again
+        issue_tile(it, kTileBytes, a.v_cache);  // the V buffer is free again
       } else {
         koff = voff = (it & 1) * kTileBytes;
         if (it + 1 < ntiles) issue_tile(it + 1, ((it + 1) & 1) * kTileBytes, a.k_cache);
       }
 
       // ---- S^T = K Q^T over this wave's four blocks, K operands prefetched
-      // two MFMA steps ahead
+      // kKPre MFMA steps ahead
       const DSA_LDS uint8_t* kt = lds + koff;
       constexpr int kSteps = 4 * kKSteps;
       auto load_k = [&](int s) -> i32x8 {
@@ -547,17 +626,18 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
         return kop;
       };
       f32x4 S[4];
-      i32x8 kbuf[3];
-      kbuf[0] = load_k(0);
-      if (kSteps > 1) kbuf[1] = load_k(1);
+      constexpr int kKPre = 3;
+      i32x8 kbuf[kKPre + 1];
+#pragma unroll
+      for (int s = 0; s < kKPre && s < kSteps; ++s) kbuf[s] = load_k(s);
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const int k = s / kKSteps, ks = s % kKSteps;
-        if (s + 2 < kSteps) kbuf[(s + 2) % 3] = load_k(s + 2);
+        if (s + kKPre < kSteps) kbuf[(s + kKPre) % (kKPre + 1)] = load_k(s + kKPre);
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        S[k] = mfma_fp8(kbuf[s % 3], qhi[ks], S[k]);
-        S[k] = mfma_fp8(kbuf[s % 3], qlo[ks], S[k]);
+        S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qhi[ks], S[k]);
+        S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qlo[ks], S[k]);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -650,18 +730,21 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
         }
         return vop;
       };
-      i32x8 vbuf[2];
-      vbuf[0] = load_v(0);
+      constexpr int kVPre = 2;
+      i32x8 vbuf[kVPre + 1];
+#pragma unroll
+      for (int j = 0; j < kVPre && j < kCB; ++j) vbuf[j] = load_v(j);
 #pragma unroll
       for (int j0 = 0; j0 < kCB; ++j0) {
-        if (j0 + 1 < kCB) vbuf[(j0 + 1) & 1] = load_v(j0 + 1);
+        if (j0 + kVPre < kCB) vbuf[(j0 + kVPre) % (kVPre + 1)] = load_v(j0 + kVPre);
         __builtin_amdgcn_sched_barrier(0);
+        const i32x8& vop = vbuf[j0 % (kVPre + 1)];
 #pragma unroll
         for (int x = 0; x < kPair; ++x)
-          O[x][j0] = mfma_fp8_bscaled(vbuf[j0 & 1], pH[x], psc[x], O[x][j0]);
+          O[x][j0] = mfma_fp8_bscaled(vop, pH[x], psc[x], O[x][j0]);
 #pragma unroll
         for (int x = 0; x < kPair; ++x)
-          O[x][j0] = mfma_fp8_bscaled(vbuf[j0 & 1], pL[x], psc[x], O[x][j0]);
+          O[x][j0] = mfma_fp8_bscaled(vop, pL[x], psc[x], O[x][j0]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -709,25 +792,32 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
     for (int x = 0; x < kPair; ++x) store_out(x, O[x], l_run[x]);
     return;
   }
-  // Partials of a workgroup: each wave's accumulators as they sit in its
-  // registers, component-major (256 contiguous bytes per store), then
-  // (reference, sum) of the block's 64 heads; all device-coherent.
+  // Split chunks. Each workgroup counts itself in; the last one to arrive
+  // merges. The others publish their partials (each wave's accumulators as
+  // they sit in its registers, 1 KiB per store, then (reference, sum) of the
+  // block's 64 heads), written through device-coherently, and count them
+  // published; the merger waits for that count. Only workgroups that have
+  // already arrived are waited for, so the wait always ends; a bounded spin
+  // turns a broken count into NaN output instead of a hang.
   constexpr int kPartFloats = kPair * kCB * kWave * 4;  // per wave
   const size_t wg_slot = (size_t)(r * a.head_blocks + hb) * a.chunks;
+  const int rh = r * a.head_blocks + hb;
+  int32_t* arrived = a.ws_arrivals + rh;
+  int32_t* published = a.ws_arrivals + (size_t)a.rows_hb + rh;
   auto part_o_of = [&](int cc) {
     return a.part_o + ((wg_slot + cc) * kWaves + wave) * kPartFloats;
   };
   auto part_ml_of = [&](int cc, int x) {
     return a.part_ml + ((wg_slot + cc) * kHeadsPerBlock + (pset * kPair + x) * 16 + li) * 2;
   };
-  {
+  if (tid == 0) flag_sh = atomicAdd(arrived, 1) == a.chunks - 1 ? 2 : 0;
+  __syncthreads();
+  if (flag_sh != 2) {
     float* po = part_o_of(c);
 #pragma unroll
     for (int x = 0; x < kPair; ++x)
 #pragma unroll
-      for (int j = 0; j < kCB; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_dev(po + ((x * kCB + j) * 4 + i) * kWave + lane, O[x][j][i]);
+      for (int j = 0; j < kCB; ++j) store_dev16(po + ((x * kCB + j) * kWave + lane) * 4, O[x][j]);
     if (jbase == 0 && g == 0)
 #pragma unroll
       for (int x = 0; x < kPair; ++x) {
@@ -735,57 +825,83 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
         store_dev(pml, m_run[x]);
         store_dev(pml + 1, l_run[x]);
       }
-  }
-  // The last chunk of this (row, head block) to arrive merges all chunks.
-  // The workgroup barrier orders every wave's partial stores before thread
-  // 0's device-scope release (one L2 write-back per workgroup, not one per
-  // wave); thread 0's acquire after the count likewise covers the loads the
-  // other waves issue after the second barrier.
-  __syncthreads();
-  if (tid == 0) {
-    int32_t* ctr = &a.ws_arrivals[r * a.head_blocks + hb];
-    __threadfence();
-    const int old = atomicAdd(ctr, 1);
-    const bool last = old == a.chunks - 1;
-    if (last) {
-      *ctr = 0;  // ready for the next launch
+    wait_vmcnt<0>();  // this wave's stores are complete before the barrier
+    __syncthreads();
+    if (tid == 0) {
       __threadfence();
+      atomicAdd(published, 1);
     }
-    flag_sh = last ? 2 : 0;
+    return;
+  }
+  if (tid == 0) {
+    constexpr int kMaxSpins = 1 << 24;
+    int spins = 0;
+    while (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               a.chunks - 1 &&
+           spins < kMaxSpins) {
+      __builtin_amdgcn_s_sleep(2);
+      ++spins;
+    }
+    flag_sh = spins < kMaxSpins ? 2 : 3;
+    // every other chunk has counted itself in and published: reset for the
+    // next launch
+    __hip_atomic_store(arrived, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __threadfence();
   }
   __syncthreads();
-  if (flag_sh != 2) return;
-  // Fixed chunk order, whichever chunk merges, so the result is deterministic.
+  const float poison = flag_sh == 2 ? 0.f : __builtin_nanf("");
+  // Online log-sum-exp merge in fixed chunk order (deterministic whichever
+  // chunk merges); each chunk's (reference, sum, partial) loads are issued
+  // together.
+  float M[kPair], Ls[kPair];
+  f32x4 acc[kPair][kCB];
 #pragma unroll
   for (int x = 0; x < kPair; ++x) {
-    float M = m_run[x];
-    for (int cc = 0; cc < a.chunks; ++cc)
-      if (cc != c) M = fmaxf(M, load_dev(part_ml_of(cc, x)));
-    f32x4 acc[kCB];
+    M[x] = -INFINITY;
+    Ls[x] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kCB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float Lsum = 0.f;
-    if (M != -INFINITY) {
-      for (int cc = 0; cc < a.chunks; ++cc) {
+    for (int j = 0; j < kCB; ++j) acc[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int cc = 0; cc < a.chunks; ++cc) {
+    float mc[kPair], lc[kPair];
+    f32x4 oc[kPair][kCB];
+    if (cc == c) {
+#pragma unroll
+      for (int x = 0; x < kPair; ++x) {
+        mc[x] = m_run[x];
+        lc[x] = l_run[x];
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) oc[x][j] = O[x][j];
+      }
+    } else {
+      const float* po = part_o_of(cc);
+#pragma unroll
+      for (int x = 0; x < kPair; ++x) {
         const float* pml = part_ml_of(cc, x);
-        const float mc = cc == c ? m_run[x] : load_dev(pml);
-        if (mc == -INFINITY) continue;  // empty chunk: its partial is zero
-        const float w = fast_exp2(mc - M);
-        Lsum += w * (cc == c ? l_run[x] : load_dev(pml + 1));
-        if (cc == c) {
+        mc[x] = pml[0];
+        lc[x] = pml[1];
 #pragma unroll
-          for (int j = 0; j < kCB; ++j) acc[j] += w * O[x][j];
-        } else {
-          const float* po = part_o_of(cc);
-#pragma unroll
-          for (int j = 0; j < kCB; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[j][i] += w * load_dev(po + ((x * kCB + j) * 4 + i) * kWave + lane);
-        }
+        for (int j = 0; j < kCB; ++j) oc[x][j] = *(const f32x4*)(po + ((x * kCB + j) * kWave + lane) * 4);
       }
     }
-    store_out(x, acc, Lsum);
+#pragma unroll
+    for (int x = 0; x < kPair; ++x) {
+      if (mc[x] == -INFINITY) continue;  // empty chunk: its partial is zero
+      const float mn = fmaxf(M[x], mc[x]);
+      const float wold = M[x] == -INFINITY ? 0.f : fast_exp2(M[x] - mn);
+      const float wnew = fast_exp2(mc[x] - mn);
+      Ls[x] = Ls[x] * wold + lc[x] * wnew;
+#pragma unroll
+      for (int j = 0; j < kCB; ++j) acc[x][j] = acc[x][j] * wold + oc[x][j] * wnew;
+      M[x] = mn;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kPair; ++x) {
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) acc[x][j] += poison;
+    store_out(x, acc[x], Ls[x]);
   }
 }
 
@@ -939,6 +1055,7 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.chunks = plan->chunks;
   da.chunk_tokens = plan->chunk_tokens;
   da.head_blocks = plan->head_blocks;
+  da.rows_hb = p.num_rows * plan->head_blocks;
   da.scale_log2 = p.sm_scale * k_scale * kLog2e;
   da.v_scale = v_scale;
   const int groups =

@@ -174,7 +174,7 @@ void plan_layout(dsa_decode_plan_s* plan) {
   L.counts = off;
   off = align_up(off + sizeof(int32_t) * R, kWsAlign);
   L.arrivals = off;
-  off = align_up(off + sizeof(int32_t) * R * plan->head_blocks, kWsAlign);
+  off = align_up(off + sizeof(int32_t) * 2 * R * plan->head_blocks, kWsAlign);
   if (plan->chunks > 1) {
     // Partials are kept per workgroup for a full block of kHeadsPerBlock
     // heads (a block that holds fewer heads still stores whole head groups).

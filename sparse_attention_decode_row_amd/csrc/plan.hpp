@@ -25,7 +25,7 @@ struct WorkspaceLayout {
   size_t ids = 0;       // int32 [R, W]
   size_t offsets = 0;   // uint64 [R, W]
   size_t counts = 0;    // int32 [R]
-  size_t arrivals = 0;  // int32 [R, head_blocks] (zero between launches)
+  size_t arrivals = 0;  // int32 [2, R, head_blocks] arrived / published counts (zero between launches)
   size_t part_o = 0;    // float [R, head_blocks, C, 64 heads, D] (C > 1 only)
   size_t part_ml = 0;   // float [R, head_blocks, C, 64 heads, 2] (C > 1 only)
   size_t total = 0;
