@@ -87,8 +87,19 @@ typedef struct dsa_decode_params {
    * Otherwise a positive multiple of 64 that forces that split (used to test
    * that the result does not depend on the split). */
   int32_t chunk_tokens;
-  int32_t reserved[4]; /* must be zero */
+  /* Work decomposition: DSA_DECODE_LAYOUT_AUTO (0) lets the planner choose
+   * (currently always the wide layout);
+   * DSA_DECODE_LAYOUT_WIDE (1): blocks of up to 64 heads, one workgroup per
+   * CU with a double-buffered tile; DSA_DECODE_LAYOUT_PAIRED (2): blocks of
+   * up to 32 heads, single-buffered, two workgroups per CU (chunks of at
+   * most 1024 selected tokens). The result does not depend on it. */
+  int32_t layout;
+  int32_t reserved[3]; /* must be zero */
 } dsa_decode_params;
+
+#define DSA_DECODE_LAYOUT_AUTO 0
+#define DSA_DECODE_LAYOUT_WIDE 1
+#define DSA_DECODE_LAYOUT_PAIRED 2
 
 /* Opaque plan: validated geometry plus the launch decomposition. Host
  * memory owned by the library; free it with dsa_decode_plan_destroy. */
@@ -99,13 +110,17 @@ typedef struct dsa_decode_plan_info {
   int32_t device;          /* HIP device id, or -1 for a host-only plan */
   int32_t chunk_tokens;    /* selected tokens per workgroup */
   int32_t chunks_per_row;  /* workgroups per row per head block */
-  int32_t head_blocks;     /* groups of up to 64 heads */
+  int32_t head_blocks;     /* groups of up to heads_per_block heads */
   int32_t workgroups;      /* rows * head_blocks * chunks_per_row */
   int32_t merges_chunks;   /* 1 when chunks_per_row > 1: the last chunk of a
                             * row to finish merges the others' partials */
   int32_t num_cus;         /* compute units the plan was sized for */
-  int32_t reserved;
+  int32_t chunk_lead;      /* extra selected tokens of chunk 0 when split (it
+                            * finishes last and merges); the last chunk has
+                            * that many fewer */
   uint64_t workspace_bytes;
+  int32_t layout;          /* DSA_DECODE_LAYOUT_WIDE or _PAIRED (resolved) */
+  int32_t heads_per_block; /* 64 or 32 */
 } dsa_decode_plan_info;
 
 /* Validate params and build a plan.
@@ -203,7 +218,7 @@ const char* dsa_decode_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 200
+#define DSA_DECODE_VERSION 210
 
 #ifdef __cplusplus
 }

@@ -60,7 +60,8 @@ class Params(ctypes.Structure):
         ("max_seq_len", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("layout", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -73,8 +74,10 @@ class PlanInfo(ctypes.Structure):
         ("workgroups", ctypes.c_int32),
         ("merges_chunks", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("chunk_lead", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_uint64),
+        ("layout", ctypes.c_int32),
+        ("heads_per_block", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -158,7 +161,7 @@ class Plan:
                  block_size: int, index_kpool: int, sel_width: int,
                  block_table_stride: int, max_seq_len: int, sm_scale: float,
                  num_kv_heads: int = 1, cache_stride_bytes: int = 0,
-                 chunk_tokens: int = 0, device: Optional[int] = None):
+                 chunk_tokens: int = 0, layout: int = 0, device: Optional[int] = None):
         if device is None:
             import torch
             device = torch.cuda.current_device()
@@ -166,7 +169,7 @@ class Plan:
         self.params = Params(num_rows, num_q_heads, num_kv_heads, kv_lora_rank,
                              block_size, index_kpool, sel_width, block_table_stride,
                              cache_stride_bytes, max_seq_len, sm_scale, chunk_tokens,
-                             (ctypes.c_int32 * 4)(0, 0, 0, 0))
+                             layout, (ctypes.c_int32 * 3)(0, 0, 0))
         h = ctypes.c_void_p()
         _check(self._lib.dsa_decode_plan(ctypes.byref(self.params), int(device),
                                          ctypes.byref(h)))

@@ -232,7 +232,9 @@ struct DecodeArgs {
   int block_size;
   int chunks;
   int chunk_tokens;
+  int chunk_lead;    // extra tokens of chunk 0 (ranks shift by this for c > 0)
   int head_blocks;
+  int heads_per_block;  // 64, or 32 with two workgroups per CU
   int rows_hb;       // R * head_blocks (stride between the two counter arrays)
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
@@ -241,13 +243,20 @@ struct DecodeArgs {
 // kGroups: 16-head groups per workgroup (1, 2 or 4); two waves per group.
 // kSplitV: V is read from its own buffer (K and V tiles staged side by side,
 // single-buffered, K of the next tile loading during PV and V during QK).
-// Otherwise K and V are the same bytes and the tile buffer is doubled.
-template <int D, int kGroups, bool kSplitV>
-__global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(DecodeArgs a) {
+// Otherwise K and V are the same bytes and kStages tile buffers hold them:
+// two (the next tile loads while one is consumed; one workgroup per CU), or
+// one (the tile loads between consumptions; under 80 KiB of LDS, so two
+// workgroups share a CU and each one's loads and softmax overlap the other's
+// matrix work).
+template <int D, int kGroups, bool kSplitV, int kStages>
+__global__ __launch_bounds__(2 * kGroups * kWave, kStages == 1 ? 2 : 1)
+void dsa_decode_kernel(DecodeArgs a) {
+  static_assert(kStages == 2 || (kStages == 1 && !kSplitV), "one stage holds K and V only when they are the same bytes");
   constexpr int kWaves = 2 * kGroups;
   constexpr int kThreads = kWave * kWaves;
   constexpr int kTileBytes = kTile * D;
-  constexpr int kSmemBytes = 2 * kTileBytes;        // two stages, or K + V
+  constexpr int kSmemBytes = (kSplitV ? 2 : kStages) * kTileBytes;
+  constexpr int kRowsCap = kStages == 2 ? kMaxChunkTokens : kMaxChunkTokens / 2;
   constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
   // PV: a wave accumulates kPair head groups over a 1/kCS slice of the
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
                 "K operand offsets must fit the LDS instruction offset field");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
+  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kRowsCap];
   // softmax weights of a tile, [group][hi|lo][token half][lane] x 4 blocks
   __shared__ __attribute__((aligned(16))) i32x4 xch_p[kGroups][2][2][kWave];
   __shared__ int xch_e[kGroups][2][kWave];   // their E8M0 exponent bytes
@@ -291,15 +300,18 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
   const int hb = wg % a.head_blocks;
   const int r = wg / a.head_blocks;
 
-  const int head = hb * kHeadsPerBlock + hg * 16 + li;
+  const int head = hb * a.heads_per_block + hg * 16 + li;
   const bool head_ok = head < a.H;
 
 
   // ------------------------------------------------------------ 1. selection
   // Membership bitmap over one window of positions at a time (the tile
   // buffers are free until the first DMA). The workgroup keeps the ids of
-  // ascending rank cstart .. cend - 1.
-  const int cstart = c * a.chunk_tokens, cend = cstart + a.chunk_tokens;
+  // ascending rank cstart .. cend - 1. Chunk 0 takes chunk_lead extra ranks:
+  // it finishes last and merges, by which time the other chunks' partials
+  // are out.
+  const int cstart = c * a.chunk_tokens + (c > 0 ? a.chunk_lead : 0);
+  const int cend = (c + 1) * a.chunk_tokens + a.chunk_lead;
   const int32_t* srow = a.sel + (size_t)r * a.width;
   // The length and up to 4 ids per thread are loaded first, from addresses
   // clamped into their buffers (no branches); the query is loaded only once
@@ -316,11 +328,14 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
   // This wave's share of the query: head li, latent columns 128*ks + 32*g +
   // [0, 32). With several k-steps a wave takes ks = 2*i + hf, the other wave
   // of the group converts the rest and the two exchange the FP8 terms
-  // through the second tile buffer (4 KiB per group and k-step: exactly one
-  // buffer at four groups); a single k-step is loaded by both waves.
+  // through tile buffer memory not yet in use (4 KiB per group and k-step:
+  // exactly one tile at four groups); a single k-step is loaded by both waves.
   constexpr bool kShareQ = kKSteps >= 2;
   constexpr int kKOwn = kShareQ ? (kKSteps + 1) / 2 : kKSteps;
   static_assert(!kShareQ || kGroups * kKSteps * 4096 <= kTileBytes, "query exchange area");
+  // the second buffer, or with a single one the buffer itself (its first
+  // tile is issued inside the loop, after the exchange has been read)
+  constexpr int kQxOff = kSmemBytes > kTileBytes ? kTileBytes : 0;
   auto own_ks = [&](int i) { return kShareQ ? 2 * i + hf : i; };
   u32x4 qraw[kKOwn][4];
   auto load_q = [&]() {
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
     __syncthreads();  // the bitmap and scan_sh are reused by the next window
   }
   if (!q_loaded) load_q();
-  const int n = max(0, min(a.chunk_tokens, total - cstart));
+  const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
 
   // ids -> latent row indices (page * rows per page + slot in page), four
@@ -471,7 +486,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
     int sh = 7 - e;
     sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
     const float qs = pow2i(sh);
-    u32x4* qx = (u32x4*)(smem + kTileBytes);  // [group][ks][hi|lo][half][lane]
+    u32x4* qx = (u32x4*)(smem + kQxOff);  // [group][ks][hi|lo][half][lane]
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
       const int ks = own_ks(i);
@@ -534,10 +549,10 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
   // Tile 0's K (and, when K and V are the same bytes, its V) goes out now;
   // a separate V buffer is filled at the top of the first tile, after every
   // wave has read its query terms out of it.
-  if (ntiles > 0) issue_tile(0, 0, a.k_cache);
+  if (kStages == 2 && ntiles > 0) issue_tile(0, 0, a.k_cache);
 
   if constexpr (kShareQ) {
-    const u32x4* qx = (const u32x4*)(smem + kTileBytes);
+    const u32x4* qx = (const u32x4*)(smem + kQxOff);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
@@ -593,13 +608,19 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
       for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
     bool overflow = false;
-    if (pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
+    if (kStages == 2 && pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
 
     for (int it = 0; it < ntiles; ++it) {
+      if constexpr (kStages == 1) {
+        barrier_lds();  // every wave is done with the buffer (PV of it-1, or the query exchange)
+        issue_tile(it, 0, a.k_cache);
+      }
       wait_vmcnt<0>();
       barrier_lds();  // tile `it` (its K half when split) is in LDS; PV of it-1 is done
       int koff, voff;
-      if constexpr (kSplitV) {
+      if constexpr (kStages == 1) {
+        koff = voff = 0;
+      } else if constexpr (kSplitV) {
         koff = 0;
         voff = kTileBytes;
         issue_tile(it, kTileBytes, a.v_cache);  // the V buffer is free again
@@ -776,7 +797,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
   // Lane holds O^T rows d = 16*(jbase + j) + 4*g + i for head li of group
   // pset*kPair + x.
   auto store_out = [&](int x, const f32x4* o, float lsum) {
-    const int hx = hb * kHeadsPerBlock + (pset * kPair + x) * 16 + li;
+    const int hx = hb * a.heads_per_block + (pset * kPair + x) * 16 + li;
     if (hx >= a.H) return;
     const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
     uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
@@ -808,7 +829,7 @@ __global__ __launch_bounds__(2 * kGroups * kWave, 1) void dsa_decode_kernel(Deco
     return a.part_o + ((wg_slot + cc) * kWaves + wave) * kPartFloats;
   };
   auto part_ml_of = [&](int cc, int x) {
-    return a.part_ml + ((wg_slot + cc) * kHeadsPerBlock + (pset * kPair + x) * 16 + li) * 2;
+    return a.part_ml + ((wg_slot + cc) * a.heads_per_block + (pset * kPair + x) * 16 + li) * 2;
   };
   if (tid == 0) flag_sh = atomicAdd(arrived, 1) == a.chunks - 1 ? 2 : 0;
   __syncthreads();
@@ -916,22 +937,25 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int kGroups>
-hipError_t launch_g(bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+hipError_t launch_g(bool split_v, int stages, dim3 grid, hipStream_t st, const DecodeArgs& args) {
   const dim3 block(2 * kGroups * kWave);
   if (split_v)
-    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true, 2>), grid, block, 0, st, args);
+  else if (stages == 1 && kGroups <= 2)
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups <= 2 ? kGroups : 2, false, 1>), grid, block, 0,
+                       st, args);
   else
-    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false, 2>), grid, block, 0, st, args);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int groups, bool split_v, dim3 grid, hipStream_t st,
+hipError_t launch_d(int groups, bool split_v, int stages, dim3 grid, hipStream_t st,
                     const DecodeArgs& args) {
   switch (groups) {
-    case 1: return launch_g<D, 1>(split_v, grid, st, args);
-    case 2: return launch_g<D, 2>(split_v, grid, st, args);
-    default: return launch_g<D, 4>(split_v, grid, st, args);
+    case 1: return launch_g<D, 1>(split_v, stages, grid, st, args);
+    case 2: return launch_g<D, 2>(split_v, stages, grid, st, args);
+    default: return launch_g<D, 4>(split_v, stages, grid, st, args);
   }
 }
 
@@ -1054,20 +1078,22 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.block_size = p.block_size;
   da.chunks = plan->chunks;
   da.chunk_tokens = plan->chunk_tokens;
+  da.chunk_lead = plan->chunk_lead;
   da.head_blocks = plan->head_blocks;
+  da.heads_per_block = plan->heads_per_block;
   da.rows_hb = p.num_rows * plan->head_blocks;
   da.scale_log2 = p.sm_scale * k_scale * kLog2e;
   da.v_scale = v_scale;
-  const int groups =
-      head_groups(p.num_q_heads < kHeadsPerBlock ? p.num_q_heads : kHeadsPerBlock);
+  const int hpb = plan->heads_per_block;
+  const int groups = head_groups(p.num_q_heads < hpb ? p.num_q_heads : hpb);
   const bool split_v = k_cache != v_cache;
   const dim3 grid(p.num_rows * plan->head_blocks * plan->chunks);
   hipError_t e;
   switch (p.kv_lora_rank) {
-    case 64: e = launch_d<64>(groups, split_v, grid, stream_h, da); break;
-    case 128: e = launch_d<128>(groups, split_v, grid, stream_h, da); break;
-    case 256: e = launch_d<256>(groups, split_v, grid, stream_h, da); break;
-    default: e = launch_d<512>(groups, split_v, grid, stream_h, da); break;
+    case 64: e = launch_d<64>(groups, split_v, plan->stages, grid, stream_h, da); break;
+    case 128: e = launch_d<128>(groups, split_v, plan->stages, grid, stream_h, da); break;
+    case 256: e = launch_d<256>(groups, split_v, plan->stages, grid, stream_h, da); break;
+    default: e = launch_d<512>(groups, split_v, plan->stages, grid, stream_h, da); break;
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,

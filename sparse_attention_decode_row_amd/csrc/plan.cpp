@@ -125,9 +125,18 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
       << kMaxChunkTokens;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 3; ++i)
     if (p->reserved[i] != 0)
       return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
+  if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_PAIRED) {
+    m << "dsa_decode_plan: layout " << p->layout << " is not 0 (auto), 1 (wide) or 2 (paired)";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->layout == DSA_DECODE_LAYOUT_PAIRED && p->chunk_tokens > kMaxChunkTokens / 2) {
+    m << "dsa_decode_plan: chunk_tokens " << p->chunk_tokens
+      << " exceeds " << kMaxChunkTokens / 2 << " for the paired layout";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
   // Offsets into the selection, q and out are formed in 64-bit arithmetic
   // on the device; the per-row element counts must fit 32 bits.
   if ((int64_t)p->num_q_heads * p->kv_lora_rank > INT32_MAX) {
@@ -143,7 +152,19 @@ void plan_layout(dsa_decode_plan_s* plan) {
   const dsa_decode_params& p = plan->p;
   const int64_t R = p.num_rows, H = p.num_q_heads, D = p.kv_lora_rank,
                 W = p.sel_width;
-  plan->head_blocks = (int)((H + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  // Paired layout: 32-head blocks, one tile buffer, two workgroups per CU.
+  // Measured on MI355X at the long-context shape it loses to the wide layout
+  // (each tile's gather latency is exposed and the co-resident workgroup
+  // does not hide it), so the planner picks the wide layout by itself.
+  int layout = p.layout;
+  if (layout == DSA_DECODE_LAYOUT_AUTO) layout = DSA_DECODE_LAYOUT_WIDE;
+  plan->layout = layout;
+  const bool paired = layout == DSA_DECODE_LAYOUT_PAIRED;
+  plan->heads_per_block = paired ? kHeadsPerPairedBlock : kHeadsPerBlock;
+  plan->stages = paired ? 1 : 2;
+  plan->max_chunk = paired ? kMaxChunkTokens / 2 : kMaxChunkTokens;
+  const int64_t wg_target = (int64_t)plan->num_cus * (paired ? 2 : 1);
+  plan->head_blocks = (int)((H + plan->heads_per_block - 1) / plan->heads_per_block);
   // A row can attend at most min(W, max_seq_len) distinct tokens.
   const int64_t wmax = std::min<int64_t>(W, p.max_seq_len);
   int64_t ct;
@@ -154,16 +175,25 @@ void plan_layout(dsa_decode_plan_s* plan) {
     // tokens one workgroup should take so that rows x head blocks x chunks
     // is about one workgroup per CU.
     const int64_t units = R * plan->head_blocks;
-    int64_t per_cu = (wmax * units + plan->num_cus - 1) / plan->num_cus;
-    ct = (per_cu + kTileTokens - 1) / kTileTokens * kTileTokens;
+    int64_t per_wg = (wmax * units + wg_target - 1) / wg_target;
+    ct = (per_wg + kTileTokens - 1) / kTileTokens * kTileTokens;
     ct = std::max<int64_t>(ct, kTileTokens);
-    ct = std::min<int64_t>(ct, kMaxChunkTokens);
+    ct = std::min<int64_t>(ct, plan->max_chunk);
   }
   const int64_t wmax_tiles = (wmax + kTileTokens - 1) / kTileTokens * kTileTokens;
   ct = std::min<int64_t>(ct, std::max<int64_t>(wmax_tiles, kTileTokens));
   plan->chunk_tokens = (int)ct;
   plan->chunks = (int)((wmax + ct - 1) / ct);
   if (plan->chunks < 1) plan->chunks = 1;
+  // With several chunks the last one to finish merges the others' partials.
+  // Giving chunk 0 one more 128-token tile (and the last chunk one fewer)
+  // makes chunk 0 that last one, so the others publish their partials while
+  // it still computes. The rank ranges still cover [0, chunks * ct).
+  plan->chunk_lead = 0;
+  if (plan->chunks > 1 && p.chunk_tokens == 0) {
+    const int64_t lead = std::min<int64_t>(2 * kTileTokens, plan->max_chunk - ct);
+    if (lead > 0 && ct > lead) plan->chunk_lead = (int)lead;
+  }
 
   WorkspaceLayout& L = plan->ws;
   size_t off = 0;
@@ -176,9 +206,9 @@ void plan_layout(dsa_decode_plan_s* plan) {
   L.arrivals = off;
   off = align_up(off + sizeof(int32_t) * 2 * R * plan->head_blocks, kWsAlign);
   if (plan->chunks > 1) {
-    // Partials are kept per workgroup for a full block of kHeadsPerBlock
+    // Partials are kept per workgroup for a full block of heads_per_block
     // heads (a block that holds fewer heads still stores whole head groups).
-    const int64_t slots = R * plan->head_blocks * plan->chunks * kHeadsPerBlock;
+    const int64_t slots = R * plan->head_blocks * plan->chunks * plan->heads_per_block;
     L.part_o = off;
     off = align_up(off + sizeof(float) * slots * D, kWsAlign);
     L.part_ml = off;
@@ -258,7 +288,9 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->workgroups = plan->p.num_rows * plan->head_blocks * plan->chunks;
   info->merges_chunks = plan->chunks > 1 ? 1 : 0;
   info->num_cus = plan->num_cus;
-  info->reserved = 0;
+  info->chunk_lead = plan->chunk_lead;
+  info->layout = plan->layout;
+  info->heads_per_block = plan->heads_per_block;
   info->workspace_bytes = plan->ws.total;
   return DSA_DECODE_OK;
 }

@@ -16,8 +16,10 @@ constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
 // Largest chunk one workgroup handles (its latent-row table lives in LDS:
 // 2048 x 4 B = 8 KiB).
 constexpr int kMaxChunkTokens = 2048;
-// Heads one workgroup covers (4 groups of 16 heads, two waves per group).
+// Heads one workgroup covers: 4 groups of 16 heads (two waves per group) in
+// the wide layout, 2 groups in the paired one.
 constexpr int kHeadsPerBlock = 64;
+constexpr int kHeadsPerPairedBlock = 32;
 // Workspace sub-buffer alignment.
 constexpr size_t kWsAlign = 256;
 
@@ -39,7 +41,12 @@ struct dsa_decode_plan_s {
   int num_cus = 256;
   int chunk_tokens = 0;           // multiple of kTileTokens, <= kMaxChunkTokens
   int chunks = 1;                 // per row per head block
+  int chunk_lead = 0;             // extra tokens of chunk 0 (multiple of kTileTokens)
   int head_blocks = 1;
+  int heads_per_block = dsa::kHeadsPerBlock;
+  int layout = DSA_DECODE_LAYOUT_WIDE;
+  int stages = 2;                 // tile buffers per workgroup (1: paired)
+  int max_chunk = dsa::kMaxChunkTokens;
   dsa::WorkspaceLayout ws;
   // benchmark timing (dsa_decode_timing_begin / _end)
   std::vector<void*> events;      // hipEvent_t, 2 per recorded launch

@@ -145,6 +145,25 @@ def test_random_shapes(H, case):
     assert err.max() <= H.TOL
 
 
+@pytest.mark.parametrize("layout", [1, 2])
+def test_both_layouts_match_the_oracle(H, layout):
+    """The wide layout (64-head blocks, double-buffered tile) and the paired
+    one (32-head blocks, single-buffered, two workgroups per CU) compute the
+    same decode; run each on a split, multi-block shape."""
+    rng = np.random.default_rng(40 + layout)
+    wl = WL.random_case(rng, rows=5, heads=96, D=512, block_size=64, max_len=4000,
+                        width=1800)
+    _announce("layout", layout=layout)
+    for ct in (0, 384):
+        run = H.run_gpu(wl, chunk_tokens=ct, layout=layout)
+        assert run.info["layout"] == layout
+        H.check_selection(wl, run)
+        want = H.oracle_rows(wl, range(wl.rows))
+        err = H.normwise_err(run.out, want)
+        print(f"layout {layout} chunk {ct}: plan {run.info} max err {err.max():.3e}")
+        assert err.max() <= H.TOL
+
+
 def test_split_invariance(H):
     rng = np.random.default_rng(42)
     wl = WL.random_case(rng, rows=3, heads=64, D=512, block_size=64,
