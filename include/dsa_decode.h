@@ -87,19 +87,19 @@ typedef struct dsa_decode_params {
    * Otherwise a positive multiple of 64 that forces that split (used to test
    * that the result does not depend on the split). */
   int32_t chunk_tokens;
-  /* Work decomposition: DSA_DECODE_LAYOUT_AUTO (0) lets the planner choose
-   * (currently always the wide layout);
-   * DSA_DECODE_LAYOUT_WIDE (1): blocks of up to 64 heads, one workgroup per
-   * CU with a double-buffered tile; DSA_DECODE_LAYOUT_PAIRED (2): blocks of
-   * up to 32 heads, single-buffered, two workgroups per CU (chunks of at
-   * most 1024 selected tokens). The result does not depend on it. */
+  /* Heads per workgroup: DSA_DECODE_LAYOUT_AUTO (0) lets the planner choose
+   * (16 when num_q_heads <= 16, else 32); DSA_DECODE_LAYOUT_HEADS32 (1):
+   * blocks of up to 32 heads, eight waves per workgroup;
+   * DSA_DECODE_LAYOUT_HEADS16 (2): blocks of up to 16 heads, four waves.
+   * The head blocks of a row read the same latent rows through the same L2.
+   * The result does not depend on it. */
   int32_t layout;
   int32_t reserved[3]; /* must be zero */
 } dsa_decode_params;
 
 #define DSA_DECODE_LAYOUT_AUTO 0
-#define DSA_DECODE_LAYOUT_WIDE 1
-#define DSA_DECODE_LAYOUT_PAIRED 2
+#define DSA_DECODE_LAYOUT_HEADS32 1
+#define DSA_DECODE_LAYOUT_HEADS16 2
 
 /* Opaque plan: validated geometry plus the launch decomposition. Host
  * memory owned by the library; free it with dsa_decode_plan_destroy. */
@@ -111,7 +111,8 @@ typedef struct dsa_decode_plan_info {
   int32_t chunk_tokens;    /* selected tokens per workgroup */
   int32_t chunks_per_row;  /* workgroups per row per head block */
   int32_t head_blocks;     /* groups of up to heads_per_block heads */
-  int32_t workgroups;      /* rows * head_blocks * chunks_per_row */
+  int32_t workgroups;      /* launched: rows * chunks_per_row rounded up to
+                            * a multiple of 8, times head_blocks */
   int32_t merges_chunks;   /* 1 when chunks_per_row > 1: the last chunk of a
                             * row to finish merges the others' partials */
   int32_t num_cus;         /* compute units the plan was sized for */
@@ -119,8 +120,8 @@ typedef struct dsa_decode_plan_info {
                             * finishes last and merges); the last chunk has
                             * that many fewer */
   uint64_t workspace_bytes;
-  int32_t layout;          /* DSA_DECODE_LAYOUT_WIDE or _PAIRED (resolved) */
-  int32_t heads_per_block; /* 64 or 32 */
+  int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32 or _HEADS16 (resolved) */
+  int32_t heads_per_block; /* 32 or 16 */
 } dsa_decode_plan_info;
 
 /* Validate params and build a plan.
@@ -218,7 +219,7 @@ const char* dsa_decode_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 210
+#define DSA_DECODE_VERSION 300
 
 #ifdef __cplusplus
 }

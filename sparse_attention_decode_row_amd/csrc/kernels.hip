@@ -91,6 +91,13 @@ __device__ __forceinline__ void dma16(const void* g, DSA_LDS void* l_base) {
                :: "v"(g), "s"(m0v) : "memory", "m0");
 }
 
+// Same with 4 bytes per lane: lane l's word lands at l_base + 4*l.
+__device__ __forceinline__ void dma4(const void* g, DSA_LDS void* l_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(g), "s"(m0v) : "memory", "m0");
+}
+
 // Workgroup barrier that does not wait for outstanding global/DMA loads
 // (a plain __syncthreads would drain the prefetch pipeline). LDS reads and
 // writes issued before it are complete once every wave arrives.
@@ -222,100 +229,110 @@ struct DecodeArgs {
   uint64_t* ws_offsets;  // [R, W] their latent-row byte offsets (exported)
   int32_t* ws_counts;    // [R]
   int32_t* ws_arrivals;  // [2][R * head_blocks] chunks arrived / partials published; reset by the merger
-  float* part_o;         // [R, C, H, D]
-  float* part_ml;        // [R, C, H, 2]
+  float* part_o;         // [R, head_blocks, C, heads_per_block, D] (per-wave register order)
+  float* part_ml;        // [R, head_blocks, C, heads_per_block, 2]
   uint32_t stride_rows;  // cache_stride_bytes / D
+  int rows;
   int H;
   int width;
   int max_seq_len;
   int bt_stride;
+  int bt_entries;    // block-table entries a row needs: ceil(max_seq_len / block_size)
   int block_size;
   int chunks;
   int chunk_tokens;
   int chunk_lead;    // extra tokens of chunk 0 (ranks shift by this for c > 0)
   int head_blocks;
-  int heads_per_block;  // 64, or 32 with two workgroups per CU
+  int heads_per_block;  // 16 * kGroups
   int rows_hb;       // R * head_blocks (stride between the two counter arrays)
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
 };
 
-// kGroups: 16-head groups per workgroup (1, 2 or 4); two waves per group.
-// kSplitV: V is read from its own buffer (K and V tiles staged side by side,
-// single-buffered, K of the next tile loading during PV and V during QK).
-// Otherwise K and V are the same bytes and kStages tile buffers hold them:
-// two (the next tile loads while one is consumed; one workgroup per CU), or
-// one (the tile loads between consumptions; under 80 KiB of LDS, so two
-// workgroups share a CU and each one's loads and softmax overlap the other's
-// matrix work).
-template <int D, int kGroups, bool kSplitV, int kStages>
-__global__ __launch_bounds__(2 * kGroups * kWave, kStages == 1 ? 2 : 1)
+// Waves per 16-head group: in the scoring step each takes a quarter (32
+// tokens) of the 128-token tile, so that the four quarters' weights are the
+// four exponent blocks of one PV operand.
+constexpr int kParts = 4;
+
+// kGroups: 16-head groups per workgroup (1 or 2), kParts waves per group.
+// kSplitV: V is read from its own buffer (K and V tiles side by side,
+// single-buffered: K of the next tile loads during PV, V during QK).
+// Otherwise K and V are the same bytes and two tile buffers alternate: the
+// next tile loads while one is consumed.
+template <int D, int kGroups, bool kSplitV>
+__global__ __launch_bounds__(kParts * kGroups * kWave, 1)
 void dsa_decode_kernel(DecodeArgs a) {
-  static_assert(kStages == 2 || (kStages == 1 && !kSplitV), "one stage holds K and V only when they are the same bytes");
-  constexpr int kWaves = 2 * kGroups;
+  constexpr int kWaves = kParts * kGroups;
   constexpr int kThreads = kWave * kWaves;
   constexpr int kTileBytes = kTile * D;
-  constexpr int kSmemBytes = (kSplitV ? 2 : kStages) * kTileBytes;
-  constexpr int kRowsCap = kStages == 2 ? kMaxChunkTokens : kMaxChunkTokens / 2;
+  constexpr int kSmemBytes = 2 * kTileBytes;
   constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
-  // PV: a wave accumulates kPair head groups over a 1/kCS slice of the
-  // latent columns, so each V operand read feeds 2*kPair MFMAs.
-  constexpr int kPair = kGroups >= 2 ? 2 : 1;
+  // PV: a wave accumulates kPair head groups over kCB column blocks, so each
+  // V operand read feeds 2*kPair MFMAs.
+  constexpr int kPair = (kGroups == 2 && kDBlocks >= kWaves) ? 2 : 1;
   constexpr int kPairs = kGroups / kPair;           // PV head sets
-  constexpr int kCS = kWaves / kPairs;              // column slices
-  constexpr int kCB = kDBlocks / kCS;               // column blocks per PV wave
+  constexpr int kCB = kPairs * kDBlocks / kWaves;   // column blocks per PV wave
   constexpr int kChunkMask = (kDBlocks < 16 ? kDBlocks : 16) - 1;
-  constexpr int kLanesPerTok = D / 16;              // DMA lanes per latent row
+  // Gather: a latent row is D/16 lanes of 16 bytes.
+  constexpr int kLanesPerTok = D / 16;
   constexpr int kTokPerInstr = kWave / kLanesPerTok;
   constexpr int kTPW = kTile / kWaves;              // tokens each wave DMAs per tile
   constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per wave per tile
-  constexpr int kBitmapWords = kSmemBytes / 4;
+  // Selection: before the first tile the tile buffers hold the membership
+  // bitmap of a window of positions (a quarter), each word's rank (a
+  // quarter) and the row's block-table entries (the upper half).
+  constexpr int kWinWords = kSmemBytes / 16;
+  constexpr int kBtCap = kSmemBytes / 8;
+  static_assert(kCB >= 1 && kPairs * kDBlocks == kCB * kWaves, "PV column split");
   static_assert(kInstr >= 1 && kInstr * kTokPerInstr == kTPW, "DMA split");
-  static_assert(kCB >= 1, "each wave needs at least one column block");
-  static_assert(16 * 7 * D + 256 * ((kKSteps - 1) >> 1) < 65536,
+  static_assert(kBtCap % kWave == 0 && kWinWords % 4 == 0, "selection areas");
+  static_assert(16 * D + 256 * ((kKSteps - 1) >> 1) < 65536,
                 "K operand offsets must fit the LDS instruction offset field");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kRowsCap];
-  // softmax weights of a tile, [group][hi|lo][token half][lane] x 4 blocks
-  __shared__ __attribute__((aligned(16))) i32x4 xch_p[kGroups][2][2][kWave];
-  __shared__ int xch_e[kGroups][2][kWave];   // their E8M0 exponent bytes
-  __shared__ float xch_f[kWaves][kWave];     // per-head scalars between the two waves
-  __shared__ float xch_m[kGroups][kWave];    // per-head reference, for the PV waves
+  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
+  // softmax weights of a tile, [group][quarter][hi|lo][head][lane group] x 8 bytes
+  __shared__ __attribute__((aligned(16))) i32x2 xch_p[kGroups][kParts][2][16][4];
+  __shared__ int xch_e[kGroups][kParts][16];  // their E8M0 exponent bytes, per head
+  __shared__ float xch_f[kWaves][kWave];      // per-head scalars between the waves of a group
+  __shared__ float xch_m[kGroups][kWave];     // per-head reference, for the PV waves
   __shared__ int scan_sh[kWaves];
   __shared__ int flag_sh;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int g = lane >> 4, li = lane & 15;
-  // QK role: head group hg, token half hf of each tile. PV role: head groups
+  // QK role: head group hg, tile quarter `part`. PV role: head groups
   // pset*kPair + x (x < kPair), column blocks jbase .. jbase + kCB - 1.
-  const int hg = wave % kGroups, hf = wave / kGroups;
-  const int mate = hg + kGroups * (1 - hf);  // the other QK wave of the group
+  const int hg = wave % kGroups, part = wave / kGroups;
   const int pset = wave % kPairs, jbase = (wave / kPairs) * kCB;
 
-  int wg = blockIdx.x;
-  const int c = wg % a.chunks;
-  wg /= a.chunks;
-  const int hb = wg % a.head_blocks;
-  const int r = wg / a.head_blocks;
+  // Workgroup -> (row, chunk, head block). The head blocks of one (row,
+  // chunk) read the same latent rows, so they get ids 8 apart: the same XCD
+  // (ids are dealt to the 8 XCDs round-robin) and its L2 serves the second
+  // read.
+  const int bid = blockIdx.x;
+  const int hb = (bid >> 3) % a.head_blocks;
+  const int rc = (bid / (8 * a.head_blocks)) * 8 + (bid & 7);
+  if (rc >= a.rows * a.chunks) return;  // grid padding
+  const int r = rc / a.chunks, c = rc % a.chunks;
 
   const int head = hb * a.heads_per_block + hg * 16 + li;
   const bool head_ok = head < a.H;
-
+  DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
 
   // ------------------------------------------------------------ 1. selection
-  // Membership bitmap over one window of positions at a time (the tile
-  // buffers are free until the first DMA). The workgroup keeps the ids of
-  // ascending rank cstart .. cend - 1. Chunk 0 takes chunk_lead extra ranks:
-  // it finishes last and merges, by which time the other chunks' partials
-  // are out.
+  // Membership bitmap over one window of positions at a time. The workgroup
+  // keeps the ids of ascending rank cstart .. cend - 1. Chunk 0 takes
+  // chunk_lead extra ranks: it finishes last and merges, by which time the
+  // other chunks' partials are out.
   const int cstart = c * a.chunk_tokens + (c > 0 ? a.chunk_lead : 0);
   const int cend = (c + 1) * a.chunk_tokens + a.chunk_lead;
   const int32_t* srow = a.sel + (size_t)r * a.width;
   // The length and up to 4 ids per thread are loaded first, from addresses
-  // clamped into their buffers (no branches); the query is loaded only once
-  // the ids are in, so that its traffic does not delay them.
+  // clamped into their buffers (no branches), then the row's block-table
+  // entries go straight into LDS; the query is loaded only once the ids are
+  // in, so that its traffic does not delay them.
   int L = a.seq_lens[r];
   int tpre[4];  // ids tid + u*kThreads (u < 4); the rest of a wider row is loaded per window
 #pragma unroll
@@ -323,22 +340,24 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     if (tid + u * kThreads >= a.width) tpre[u] = -1;
+  const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
+  const int nbt = min(a.bt_entries, kBtCap);
+  for (int i = wave; i * kWave < nbt; i += kWaves)
+    dma4(bt + min(i * kWave + lane, nbt - 1), (DSA_LDS void*)(lds + kSmemBytes / 2 + i * 4 * kWave));
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
 
   // This wave's share of the query: head li, latent columns 128*ks + 32*g +
-  // [0, 32). With several k-steps a wave takes ks = 2*i + hf, the other wave
-  // of the group converts the rest and the two exchange the FP8 terms
-  // through tile buffer memory not yet in use (4 KiB per group and k-step:
-  // exactly one tile at four groups); a single k-step is loaded by both waves.
+  // [0, 32). With several k-steps the four waves of a group take k-steps
+  // ks = 4*i + part and exchange the FP8 terms through tile buffer memory
+  // not yet in use (4 KiB per group and k-step); a single k-step is loaded
+  // by every wave.
   constexpr bool kShareQ = kKSteps >= 2;
-  constexpr int kKOwn = kShareQ ? (kKSteps + 1) / 2 : kKSteps;
+  constexpr int kKOwn = kShareQ ? (kKSteps + kParts - 1) / kParts : kKSteps;
   static_assert(!kShareQ || kGroups * kKSteps * 4096 <= kTileBytes, "query exchange area");
-  // the second buffer, or with a single one the buffer itself (its first
-  // tile is issued inside the loop, after the exchange has been read)
-  constexpr int kQxOff = kSmemBytes > kTileBytes ? kTileBytes : 0;
-  auto own_ks = [&](int i) { return kShareQ ? 2 * i + hf : i; };
+  auto own_ks = [&](int i) { return kShareQ ? kParts * i + part : i; };
   u32x4 qraw[kKOwn][4];
   auto load_q = [&]() {
+    wait_vmcnt<0>();  // the block-table DMA (issued before) has landed
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (head_ok ? head : 0)) * D;
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
@@ -351,15 +370,17 @@ void dsa_decode_kernel(DecodeArgs a) {
 
   uint32_t* bitmap = (uint32_t*)smem;
   const DSA_LDS u32x4* bitmap4 = (const DSA_LDS u32x4*)smem;
+  const DSA_LDS uint32_t* bitmap_l = (const DSA_LDS uint32_t*)smem;
+  u32x4* wrank4 = (u32x4*)(smem + kSmemBytes / 4);
+  const DSA_LDS uint32_t* wrank_l = (const DSA_LDS uint32_t*)(smem + kSmemBytes / 4);
   if (tid == 0) flag_sh = 0;
   int total = 0;
   bool q_loaded = false;
-  for (int base = 0; base < L; base += kBitmapWords * 32) {
-    const int span = min(kBitmapWords * 32, L - base);
-    const int nwords = (span + 31) >> 5;
-    const int per = ((nwords + kThreads - 1) / kThreads + 3) & ~3;  // words per thread
-    for (int i = tid; i < per * kThreads / 4; i += kThreads)
-      ((u32x4*)bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int base = 0; base < L; base += kWinWords * 32) {
+    const int span = min(kWinWords * 32, L - base);
+    const int nw4 = (((span + 31) >> 5) + 3) & ~3;                  // words in use
+    const int per = ((nw4 / 4 + kThreads - 1) / kThreads) * 4;      // words per thread
+    for (int i = tid; i < nw4 / 4; i += kThreads) ((u32x4*)bitmap)[i] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     // a hole (any negative id) or an id outside [0, L) sets nothing
 #pragma unroll
@@ -376,10 +397,11 @@ void dsa_decode_kernel(DecodeArgs a) {
       q_loaded = true;
     }
     __syncthreads();
-    // rank of this thread's first word: wave scan, then the waves before it
-    const int w0 = tid * per;
+    // rank of each word: this thread's words are w0 .. w1 - 1; wave scan of
+    // their counts, then the waves before it
+    const int w0 = tid * per, w1 = min(w0 + per, nw4);
     int cnt = 0;
-    for (int w = w0; w < w0 + per; w += 4) {
+    for (int w = w0; w < w1; w += 4) {
       const u32x4 x = bitmap4[w >> 2];
       cnt += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
     }
@@ -393,40 +415,45 @@ void dsa_decode_kernel(DecodeArgs a) {
       all += sw;
       before += k < wave ? sw : 0;
     }
-    int rank = total + before + incl - cnt;
-    if (rank < cend && rank + cnt > cstart) {
-      for (int w = w0; w < w0 + per && rank < cend; w += 4) {
-        const u32x4 x = bitmap4[w >> 2];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          uint32_t bits = x[e];
-          const int pc = __popc(bits);
-          if (rank + pc > cstart && rank < cend) {
-            while (bits) {
-              const int b = __ffs(bits) - 1;
-              bits &= bits - 1;
-              if (rank >= cstart && rank < cend)
-                rows_lds[rank - cstart] = (uint32_t)(base + ((w + e) << 5) + b);
-              ++rank;
-            }
-          } else {
-            rank += pc;
-          }
-        }
-      }
+    int run = before + incl - cnt;
+    for (int w = w0; w < w1; w += 4) {
+      const u32x4 x = bitmap4[w >> 2];
+      u32x4 rk;
+      rk.x = (unsigned)run;
+      run += __popc(x.x);
+      rk.y = (unsigned)run;
+      run += __popc(x.y);
+      rk.z = (unsigned)run;
+      run += __popc(x.z);
+      rk.w = (unsigned)run;
+      run += __popc(x.w);
+      wrank4[w >> 2] = rk;
     }
+    __syncthreads();
+    // Each id finds its own rank: its word's rank plus the set bits below it
+    // in the word. Repeats of an id write the same entry with the same value.
+    auto place = [&](int t) {
+      if (t >= base && t - base < span) {
+        const int o = t - base, w = o >> 5;
+        const int rank = total + (int)wrank_l[w] + __popc(bitmap_l[w] & ((1u << (o & 31)) - 1u));
+        if (rank >= cstart && rank < cend) rows_lds[rank - cstart] = (uint32_t)t;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 4; ++u) place(tpre[u]);
+    for (int j = tid + 4 * kThreads; j < a.width; j += kThreads) place(srow[j]);
     total += all;
-    __syncthreads();  // the bitmap and scan_sh are reused by the next window
+    __syncthreads();  // the id table is complete; the bitmap is reused by the next window
   }
   if (!q_loaded) load_q();
   const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
 
-  // ids -> latent row indices (page * rows per page + slot in page), four
-  // lookups in flight per thread. The head-block-0 workgroups of the row
-  // export the ids and byte offsets.
+  // ids -> latent row indices (page * rows per page + slot in page) through
+  // the block-table entries in LDS (global memory for a page beyond them).
+  // The head-block-0 workgroups of the row export the ids and byte offsets.
   {
-    const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
+    const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
     const bool exporter = hb == 0;
     int32_t* idw = a.ws_ids + (size_t)r * a.width + cstart;
     uint64_t* offw = a.ws_offsets + (size_t)r * a.width + cstart;
@@ -439,7 +466,8 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         t[u] = min(max(t[u], 0), L - 1);  // a no-op for every id the bitmap produced
-        page[u] = i0 + u * kThreads < n ? (uint32_t)bt[t[u] / a.block_size] : 0u;
+        const int pi = t[u] / a.block_size;
+        page[u] = i0 + u * kThreads < n ? (uint32_t)(pi < nbt ? btl[pi] : bt[pi]) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -475,18 +503,21 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
   amax = max_xor32(max_xor16(amax));
   if constexpr (kShareQ) xch_f[wave][lane] = amax;
-  __syncthreads();  // row table written; both halves' maxima visible
+  __syncthreads();  // row table written (block-table area free); the groups' maxima visible
   // pad to whole tiles with the last real row (loaded, weighted by zero)
   if (n > 0)
     for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
   float score_scale;
   {
-    if constexpr (kShareQ) amax = fmaxf(amax, xch_f[mate][lane]);
+    if constexpr (kShareQ)
+#pragma unroll
+      for (int p = 0; p < kParts; ++p) amax = fmaxf(amax, xch_f[hg + kGroups * p][lane]);
     const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
     int sh = 7 - e;
     sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
     const float qs = pow2i(sh);
-    u32x4* qx = (u32x4*)(smem + kQxOff);  // [group][ks][hi|lo][half][lane]
+    // exchange area in the second tile buffer: [group][ks][hi|lo][half][lane]
+    u32x4* qx = (u32x4*)(smem + kTileBytes);
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
       const int ks = own_ks(i);
@@ -518,14 +549,13 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
     score_scale = a.scale_log2 * pow2i(-sh);
   }
-  __syncthreads();  // row table padded; both halves' FP8 terms visible
+  __syncthreads();  // row table padded; the groups' FP8 terms visible
 
   // -------------------------------------------------------------- 2. gather
   // Wave w moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its instruction k
   // writes kTokPerInstr consecutive LDS slots; DMA lane l carries chunk
   // l % kLanesPerTok of token w*kTPW + (l / kLanesPerTok)*kInstr + k, so a
   // lane's kInstr row indices are contiguous in the row table.
-  DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
   const DSA_LDS uint32_t* rows_l = (const DSA_LDS uint32_t*)rows_lds;
   auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
     const int j = lane / kLanesPerTok, ci = lane % kLanesPerTok;
@@ -549,10 +579,10 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Tile 0's K (and, when K and V are the same bytes, its V) goes out now;
   // a separate V buffer is filled at the top of the first tile, after every
   // wave has read its query terms out of it.
-  if (kStages == 2 && ntiles > 0) issue_tile(0, 0, a.k_cache);
+  if (ntiles > 0) issue_tile(0, 0, a.k_cache);
 
   if constexpr (kShareQ) {
-    const u32x4* qx = (const u32x4*)(smem + kQxOff);
+    const u32x4* qx = (const u32x4*)(smem + kTileBytes);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
       const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
@@ -564,8 +594,8 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   }
 
-  // K operand addresses. This wave scores blocks b = 4*hf + k (k < 4) of 16
-  // slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk position
+  // K operand addresses. This wave scores blocks b = 2*part + k (k < 2) of
+  // 16 slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk position
   // (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position is
   // 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ k) & 1)), so four per-lane
   // offsets plus compile-time immediates cover every read.
@@ -574,30 +604,33 @@ void dsa_decode_kernel(DecodeArgs a) {
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      kofs[p][h] = 64 * D * hf + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
+      kofs[p][h] = 32 * D * part + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
 
-  // V operand rows: read q (0..3) of a PV operand covers operand bytes
-  // 8q..8q+7, i.e. blocks 2q and 2q+1; lanes 2k and 2k+1 of a 16-lane group
-  // supply row k (halves 0 and 1).
+  // V operand rows. Operand bytes 8u .. 8u+7 of lane group g come from the
+  // scoring lanes of group g' = 2*(g & 1) + (u & 1) in quarter
+  // P = 2*(u >> 1) + (g >> 1): byte i is slot 32*P + 16*(i >> 2) + 4*g' +
+  // (i & 3). A transposing read hands lane li the 8 bytes of its column from
+  // 8 rows; lanes 2k and 2k+1 of the 16-lane group supply row k (column
+  // halves 0 and 1).
   int vrow[4], vswz[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rrow = li >> 1;
-    const int slot = 16 * (2 * q + (rrow >> 2)) + 4 * g + (rrow & 3);
-    vrow[q] = slot * D + 8 * (li & 1);
-    vswz[q] = tile_swizzle<D>(slot) << 4;
+  for (int u = 0; u < 4; ++u) {
+    const int P = 2 * (u >> 1) + (g >> 1), gp = 2 * (g & 1) + (u & 1), rr = li >> 1;
+    const int slot = 32 * P + 16 * (rr >> 2) + 4 * gp + (rr & 3);
+    vrow[u] = slot * D + 8 * (li & 1);
+    vswz[u] = tile_swizzle<D>(slot) << 4;
   }
 
   // -------------------------------------------------------------- 3. attend
   // The accumulators are touched only by the matrix cores inside the tile
   // loop: weights are taken against a fixed per-head reference (the first
-  // tile's max), and each 16-token x 2-lane-group block of weights carries
-  // its own E8M0 exponent, so a later score may exceed the reference by up
-  // to 2^kSlack without leaving the FP8 range or fp32 accumulation. Should a
+  // tile's max), and each quarter's 32 weights of a head carry their own
+  // E8M0 exponent, so a later score may exceed the reference by up to
+  // 2^kSlack without leaving the FP8 range or fp32 accumulation. Should a
   // score ever exceed it by more (only with pathological inputs), the chunk
   // is recomputed with the reference set to the exact maximum seen.
   f32x4 O[kPair][kCB];
-  float l_part = 0.f;        // this lane's share of sum_t 2^(s_t - m_ref)
+  float l_part = 0.f;        // this wave's share of sum_t 2^(s_t - m_ref), per head
   float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
   float m_seen = -INFINITY;  // exact max of this wave's scores so far
 
@@ -608,19 +641,13 @@ void dsa_decode_kernel(DecodeArgs a) {
       for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_part = 0.f;
     bool overflow = false;
-    if (kStages == 2 && pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
+    if (pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
 
     for (int it = 0; it < ntiles; ++it) {
-      if constexpr (kStages == 1) {
-        barrier_lds();  // every wave is done with the buffer (PV of it-1, or the query exchange)
-        issue_tile(it, 0, a.k_cache);
-      }
       wait_vmcnt<0>();
       barrier_lds();  // tile `it` (its K half when split) is in LDS; PV of it-1 is done
       int koff, voff;
-      if constexpr (kStages == 1) {
-        koff = voff = 0;
-      } else if constexpr (kSplitV) {
+      if constexpr (kSplitV) {
         koff = 0;
         voff = kTileBytes;
         issue_tile(it, kTileBytes, a.v_cache);  // the V buffer is free again
@@ -629,10 +656,10 @@ void dsa_decode_kernel(DecodeArgs a) {
         if (it + 1 < ntiles) issue_tile(it + 1, ((it + 1) & 1) * kTileBytes, a.k_cache);
       }
 
-      // ---- S^T = K Q^T over this wave's four blocks, K operands prefetched
+      // ---- S^T = K Q^T over this wave's two blocks, K operands prefetched
       // kKPre MFMA steps ahead
       const DSA_LDS uint8_t* kt = lds + koff;
-      constexpr int kSteps = 4 * kKSteps;
+      constexpr int kSteps = 2 * kKSteps;
       auto load_k = [&](int s) -> i32x8 {
         const int k = s / kKSteps, ks = s % kKSteps;
         i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -646,7 +673,7 @@ void dsa_decode_kernel(DecodeArgs a) {
         }
         return kop;
       };
-      f32x4 S[4];
+      f32x4 S[2];
       constexpr int kKPre = 3;
       i32x8 kbuf[kKPre + 1];
 #pragma unroll
@@ -662,41 +689,42 @@ void dsa_decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
 
-      // ---- weights. The lane holds head li at slots 16*(4*hf + k) + 4*g + i;
-      // joined with the lane 16 apart these 16 x 2 weights share one FP8
-      // exponent (operand bytes 16*hf .. 16*hf + 15 of lane groups g, g^1).
+      // ---- weights. The lane holds head li at slots 32*part + 16*k + 4*g +
+      // i; the wave's 32 weights of a head share one FP8 exponent.
       const int nvalid = n - it * kTile;
       if (__builtin_expect(nvalid < kTile, 0)) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < 2; ++k)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (token_of_slot(16 * (4 * hf + k) + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
+            if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
       }
       float mh = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 2; ++k)
         mh = fmaxf(mh, fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3])));
-      mh = max_xor16(mh) * score_scale;  // score_scale > 0
-      const float tmax = max_xor32(mh);
-      m_seen = fmaxf(m_seen, tmax);
+      mh = max_xor32(max_xor16(mh)) * score_scale;  // score_scale > 0
+      m_seen = fmaxf(m_seen, mh);
       if (pass == 0 && it == 0) {
-        // first tile: the reference is the tile's max over both halves of
-        // the head group (a workgroup-uniform branch: it holds a barrier)
-        xch_f[wave][lane] = tmax;
+        // first tile: the reference is the tile's max over the group's four
+        // quarters (a workgroup-uniform branch: it holds a barrier)
+        xch_f[wave][lane] = mh;
         barrier_lds();
-        m_ref = fmaxf(tmax, xch_f[mate][lane]);
+        float m = mh;
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
+        m_ref = m;
       }
-      overflow |= tmax > m_ref + kSlack;
+      overflow |= mh > m_ref + kSlack;
       const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
-      // block exponent: the block's largest weight maps to [128, 256)
+      // quarter exponent: the quarter's largest weight maps to [128, 256)
       int e = mh == -INFINITY ? 0 : (int)floorf(mh - mbase);
       e = e < -100 ? -100 : (e > 100 ? 100 : e);
       const float bsub = mbase + (float)(e - 7);
-      i32x4 phi, plo;
+      i32x2 phi, plo;
       float lsum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 2; ++k) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
@@ -707,9 +735,9 @@ void dsa_decode_kernel(DecodeArgs a) {
         plo[k] = lo;
       }
       l_part += lsum * pow2i(e - 7);
-      xch_p[hg][0][hf][lane] = phi;
-      xch_p[hg][1][hf][lane] = plo;
-      xch_e[hg][hf][lane] = e + 120;
+      xch_p[hg][part][0][li][g] = phi;
+      xch_p[hg][part][1][li][g] = plo;
+      if (g == 0) xch_e[hg][part][li] = e + 120;
 
       if constexpr (kSplitV) {
         wait_vmcnt<0>();  // V of this tile
@@ -719,35 +747,37 @@ void dsa_decode_kernel(DecodeArgs a) {
         barrier_lds();    // weights visible (the next tile stays in flight)
       }
 
-      // ---- full P^T operands of this wave's head groups and their exponents
+      // ---- full P^T operands of this wave's head groups: bytes 0-15 of lane
+      // group g from quarter g >> 1, bytes 16-31 from quarter 2 + (g >> 1),
+      // each 8 bytes of scoring lane groups 2*(g & 1) and 2*(g & 1) + 1; lane
+      // group g's scale byte is quarter g's exponent (the operand block it
+      // scales)
       i32x8 pH[kPair], pL[kPair];
       int psc[kPair];
 #pragma unroll
       for (int x = 0; x < kPair; ++x) {
         const int hx = pset * kPair + x;
-        const i32x4 h0 = xch_p[hx][0][0][lane], h1 = xch_p[hx][0][1][lane];
-        const i32x4 l0 = xch_p[hx][1][0][lane], l1 = xch_p[hx][1][1][lane];
+        const i32x4 h0 = *(const i32x4*)&xch_p[hx][g >> 1][0][li][2 * (g & 1)];
+        const i32x4 h1 = *(const i32x4*)&xch_p[hx][2 + (g >> 1)][0][li][2 * (g & 1)];
+        const i32x4 l0 = *(const i32x4*)&xch_p[hx][g >> 1][1][li][2 * (g & 1)];
+        const i32x4 l1 = *(const i32x4*)&xch_p[hx][2 + (g >> 1)][1][li][2 * (g & 1)];
         pH[x] = i32x8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
         pL[x] = i32x8{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        const int epack = xch_e[hx][0][lane] | (xch_e[hx][1][lane] << 8);
-        const int eother = partner_xor32(epack, lane);
-        psc[x] = g == 0 ? (epack & 0xff)
-               : g == 1 ? (eother & 0xff)
-               : g == 2 ? (eother >> 8) : (epack >> 8);
+        psc[x] = xch_e[hx][g][li];
       }
 
       // ---- O^T += V^T P^T over this wave's column blocks (one 128-token
       // operand per MFMA, shared by the head groups), V operands of the next
-      // block prefetched.
+      // blocks prefetched.
       const DSA_LDS uint8_t* vt = lds + voff;
       auto load_v = [&](int j0) -> i32x8 {
         i32x8 vop;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int addr = (((jbase + j0) << 4) ^ vswz[q]) + vrow[q];
+        for (int u = 0; u < 4; ++u) {
+          const int addr = (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
           const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
-          vop[2 * q] = v2.x;
-          vop[2 * q + 1] = v2.y;
+          vop[2 * u] = v2.x;
+          vop[2 * u + 1] = v2.y;
         }
         return vop;
       };
@@ -775,21 +805,28 @@ void dsa_decode_kernel(DecodeArgs a) {
       xch_f[wave][lane] = m_seen;
       __syncthreads();
       const bool redo = flag_sh != 0;
-      if (redo) m_ref = fmaxf(m_seen, xch_f[mate][lane]);
+      if (redo) {
+        float m = m_seen;
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
+        m_ref = m;
+      }
       __syncthreads();
       if (!redo) break;
     }
   }
 
-  // Weight sums and references of the PV waves' heads (both token halves).
+  // Weight sums and references of the PV waves' heads (all four quarters).
   xch_f[wave][lane] = sum_xor32(sum_xor16(l_part));
-  if (hf == 0) xch_m[hg][lane] = ntiles > 0 ? m_ref : -INFINITY;
+  if (part == 0) xch_m[hg][lane] = ntiles > 0 ? m_ref : -INFINITY;
   __syncthreads();
   float l_run[kPair], m_run[kPair];
 #pragma unroll
   for (int x = 0; x < kPair; ++x) {
     const int hx = pset * kPair + x;
-    l_run[x] = xch_f[hx][lane] + xch_f[hx + kGroups][lane];
+    l_run[x] = 0.f;
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) l_run[x] += xch_f[hx + kGroups * p][lane];
     m_run[x] = xch_m[hx][lane];
   }
 
@@ -816,7 +853,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Split chunks. Each workgroup counts itself in; the last one to arrive
   // merges. The others publish their partials (each wave's accumulators as
   // they sit in its registers, 1 KiB per store, then (reference, sum) of the
-  // block's 64 heads), written through device-coherently, and count them
+  // block's heads), written through device-coherently, and count them
   // published; the merger waits for that count. Only workgroups that have
   // already arrived are waited for, so the wait always ends; a bounded spin
   // turns a broken count into NaN output instead of a hang.
@@ -937,32 +974,19 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int kGroups>
-hipError_t launch_g(bool split_v, int stages, dim3 grid, hipStream_t st, const DecodeArgs& args) {
-  const dim3 block(2 * kGroups * kWave);
+hipError_t launch_g(bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+  const dim3 block(kParts * kGroups * kWave);
   if (split_v)
-    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true, 2>), grid, block, 0, st, args);
-  else if (stages == 1 && kGroups <= 2)
-    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups <= 2 ? kGroups : 2, false, 1>), grid, block, 0,
-                       st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
   else
-    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false, 2>), grid, block, 0, st, args);
+    hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false>), grid, block, 0, st, args);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int groups, bool split_v, int stages, dim3 grid, hipStream_t st,
-                    const DecodeArgs& args) {
-  switch (groups) {
-    case 1: return launch_g<D, 1>(split_v, stages, grid, st, args);
-    case 2: return launch_g<D, 2>(split_v, stages, grid, st, args);
-    default: return launch_g<D, 4>(split_v, stages, grid, st, args);
-  }
-}
-
-// 16-head groups a workgroup runs for a head block of this many heads.
-int head_groups(int heads_in_block) {
-  const int groups = (heads_in_block + 15) / 16;
-  return groups >= 3 ? 4 : groups;
+hipError_t launch_d(int groups, bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+  return groups == 1 ? launch_g<D, 1>(split_v, grid, st, args)
+                     : launch_g<D, 2>(split_v, grid, st, args);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -1071,10 +1095,12 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.part_o = plan->chunks > 1 ? (float*)(ws + plan->ws.part_o) : nullptr;
   da.part_ml = plan->chunks > 1 ? (float*)(ws + plan->ws.part_ml) : nullptr;
   da.stride_rows = (uint32_t)(p.cache_stride_bytes / (uint64_t)p.kv_lora_rank);
+  da.rows = p.num_rows;
   da.H = p.num_q_heads;
   da.width = p.sel_width;
   da.max_seq_len = p.max_seq_len;
   da.bt_stride = p.block_table_stride;
+  da.bt_entries = (int)(((int64_t)p.max_seq_len + p.block_size - 1) / p.block_size);
   da.block_size = p.block_size;
   da.chunks = plan->chunks;
   da.chunk_tokens = plan->chunk_tokens;
@@ -1084,16 +1110,15 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.rows_hb = p.num_rows * plan->head_blocks;
   da.scale_log2 = p.sm_scale * k_scale * kLog2e;
   da.v_scale = v_scale;
-  const int hpb = plan->heads_per_block;
-  const int groups = head_groups(p.num_q_heads < hpb ? p.num_q_heads : hpb);
+  const int groups = plan->heads_per_block / 16;
   const bool split_v = k_cache != v_cache;
-  const dim3 grid(p.num_rows * plan->head_blocks * plan->chunks);
+  const dim3 grid(plan->workgroups);
   hipError_t e;
   switch (p.kv_lora_rank) {
-    case 64: e = launch_d<64>(groups, split_v, plan->stages, grid, stream_h, da); break;
-    case 128: e = launch_d<128>(groups, split_v, plan->stages, grid, stream_h, da); break;
-    case 256: e = launch_d<256>(groups, split_v, plan->stages, grid, stream_h, da); break;
-    default: e = launch_d<512>(groups, split_v, plan->stages, grid, stream_h, da); break;
+    case 64: e = launch_d<64>(groups, split_v, grid, stream_h, da); break;
+    case 128: e = launch_d<128>(groups, split_v, grid, stream_h, da); break;
+    case 256: e = launch_d<256>(groups, split_v, grid, stream_h, da); break;
+    default: e = launch_d<512>(groups, split_v, grid, stream_h, da); break;
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,

@@ -128,13 +128,9 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
   for (int i = 0; i < 3; ++i)
     if (p->reserved[i] != 0)
       return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
-  if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_PAIRED) {
-    m << "dsa_decode_plan: layout " << p->layout << " is not 0 (auto), 1 (wide) or 2 (paired)";
-    return fail(DSA_DECODE_ERR_INVALID, m.str());
-  }
-  if (p->layout == DSA_DECODE_LAYOUT_PAIRED && p->chunk_tokens > kMaxChunkTokens / 2) {
-    m << "dsa_decode_plan: chunk_tokens " << p->chunk_tokens
-      << " exceeds " << kMaxChunkTokens / 2 << " for the paired layout";
+  if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS16) {
+    m << "dsa_decode_plan: layout " << p->layout
+      << " is not 0 (auto), 1 (32-head blocks) or 2 (16-head blocks)";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
   // Offsets into the selection, q and out are formed in 64-bit arithmetic
@@ -152,18 +148,16 @@ void plan_layout(dsa_decode_plan_s* plan) {
   const dsa_decode_params& p = plan->p;
   const int64_t R = p.num_rows, H = p.num_q_heads, D = p.kv_lora_rank,
                 W = p.sel_width;
-  // Paired layout: 32-head blocks, one tile buffer, two workgroups per CU.
-  // Measured on MI355X at the long-context shape it loses to the wide layout
-  // (each tile's gather latency is exposed and the co-resident workgroup
-  // does not hide it), so the planner picks the wide layout by itself.
+  // Blocks of 32 heads (two 16-head groups, eight waves) unless the heads
+  // fit one group. Every workgroup holds a CU's LDS, so the grid aims at one
+  // workgroup per CU.
   int layout = p.layout;
-  if (layout == DSA_DECODE_LAYOUT_AUTO) layout = DSA_DECODE_LAYOUT_WIDE;
+  if (layout == DSA_DECODE_LAYOUT_AUTO)
+    layout = H <= kHeadsPerSmallBlock ? DSA_DECODE_LAYOUT_HEADS16 : DSA_DECODE_LAYOUT_HEADS32;
   plan->layout = layout;
-  const bool paired = layout == DSA_DECODE_LAYOUT_PAIRED;
-  plan->heads_per_block = paired ? kHeadsPerPairedBlock : kHeadsPerBlock;
-  plan->stages = paired ? 1 : 2;
-  plan->max_chunk = paired ? kMaxChunkTokens / 2 : kMaxChunkTokens;
-  const int64_t wg_target = (int64_t)plan->num_cus * (paired ? 2 : 1);
+  plan->heads_per_block =
+      layout == DSA_DECODE_LAYOUT_HEADS16 ? kHeadsPerSmallBlock : kHeadsPerBlock;
+  const int64_t wg_target = plan->num_cus;
   plan->head_blocks = (int)((H + plan->heads_per_block - 1) / plan->heads_per_block);
   // A row can attend at most min(W, max_seq_len) distinct tokens.
   const int64_t wmax = std::min<int64_t>(W, p.max_seq_len);
@@ -178,7 +172,7 @@ void plan_layout(dsa_decode_plan_s* plan) {
     int64_t per_wg = (wmax * units + wg_target - 1) / wg_target;
     ct = (per_wg + kTileTokens - 1) / kTileTokens * kTileTokens;
     ct = std::max<int64_t>(ct, kTileTokens);
-    ct = std::min<int64_t>(ct, plan->max_chunk);
+    ct = std::min<int64_t>(ct, kMaxChunkTokens);
   }
   const int64_t wmax_tiles = (wmax + kTileTokens - 1) / kTileTokens * kTileTokens;
   ct = std::min<int64_t>(ct, std::max<int64_t>(wmax_tiles, kTileTokens));
@@ -191,7 +185,7 @@ void plan_layout(dsa_decode_plan_s* plan) {
   // it still computes. The rank ranges still cover [0, chunks * ct).
   plan->chunk_lead = 0;
   if (plan->chunks > 1 && p.chunk_tokens == 0) {
-    const int64_t lead = std::min<int64_t>(2 * kTileTokens, plan->max_chunk - ct);
+    const int64_t lead = std::min<int64_t>(2 * kTileTokens, kMaxChunkTokens - ct);
     if (lead > 0 && ct > lead) plan->chunk_lead = (int)lead;
   }
 
@@ -215,6 +209,9 @@ void plan_layout(dsa_decode_plan_s* plan) {
     off = align_up(off + sizeof(float) * slots * 2, kWsAlign);
   }
   L.total = off;
+  // Workgroup ids: the head blocks of one (row, chunk) are 8 apart, so the
+  // (row, chunk) count is padded to a multiple of 8 (padding ids exit).
+  plan->workgroups = (int)((R * plan->chunks + 7) / 8 * 8 * plan->head_blocks);
 }
 
 }  // namespace dsa
@@ -285,7 +282,7 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->chunk_tokens = plan->chunk_tokens;
   info->chunks_per_row = plan->chunks;
   info->head_blocks = plan->head_blocks;
-  info->workgroups = plan->p.num_rows * plan->head_blocks * plan->chunks;
+  info->workgroups = plan->workgroups;
   info->merges_chunks = plan->chunks > 1 ? 1 : 0;
   info->num_cus = plan->num_cus;
   info->chunk_lead = plan->chunk_lead;

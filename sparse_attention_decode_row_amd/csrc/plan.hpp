@@ -16,10 +16,10 @@ constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
 // Largest chunk one workgroup handles (its latent-row table lives in LDS:
 // 2048 x 4 B = 8 KiB).
 constexpr int kMaxChunkTokens = 2048;
-// Heads one workgroup covers: 4 groups of 16 heads (two waves per group) in
-// the wide layout, 2 groups in the paired one.
-constexpr int kHeadsPerBlock = 64;
-constexpr int kHeadsPerPairedBlock = 32;
+// Heads one workgroup covers: 2 groups of 16 heads (four waves per group),
+// or a single group.
+constexpr int kHeadsPerBlock = 32;
+constexpr int kHeadsPerSmallBlock = 16;
 // Workspace sub-buffer alignment.
 constexpr size_t kWsAlign = 256;
 
@@ -28,8 +28,8 @@ struct WorkspaceLayout {
   size_t offsets = 0;   // uint64 [R, W]
   size_t counts = 0;    // int32 [R]
   size_t arrivals = 0;  // int32 [2, R, head_blocks] arrived / published counts (zero between launches)
-  size_t part_o = 0;    // float [R, head_blocks, C, 64 heads, D] (C > 1 only)
-  size_t part_ml = 0;   // float [R, head_blocks, C, 64 heads, 2] (C > 1 only)
+  size_t part_o = 0;    // float [R, head_blocks, C, heads_per_block, D] (C > 1 only)
+  size_t part_ml = 0;   // float [R, head_blocks, C, heads_per_block, 2] (C > 1 only)
   size_t total = 0;
 };
 
@@ -44,9 +44,8 @@ struct dsa_decode_plan_s {
   int chunk_lead = 0;             // extra tokens of chunk 0 (multiple of kTileTokens)
   int head_blocks = 1;
   int heads_per_block = dsa::kHeadsPerBlock;
-  int layout = DSA_DECODE_LAYOUT_WIDE;
-  int stages = 2;                 // tile buffers per workgroup (1: paired)
-  int max_chunk = dsa::kMaxChunkTokens;
+  int layout = DSA_DECODE_LAYOUT_HEADS32;
+  int workgroups = 0;             // launched grid (rows x chunks padded to 8, x head blocks)
   dsa::WorkspaceLayout ws;
   // benchmark timing (dsa_decode_timing_begin / _end)
   std::vector<void*> events;      // hipEvent_t, 2 per recorded launch

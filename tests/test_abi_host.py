@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(native):
 
 
 def test_version(native):
-    assert native.lib().dsa_decode_version() == 210
+    assert native.lib().dsa_decode_version() == 300
 
 
 def plan(native, **kw):
@@ -106,10 +106,10 @@ def test_capacity_rule_boundary(native):
 
 
 @pytest.mark.parametrize("kw,chunks,ct", [
-    (dict(), 2, 1024),                                        # 128 rows
-    (dict(num_rows=32, max_seq_len=8192, block_table_stride=128), 8, 256),
+    (dict(), 1, 2048),                                        # 128 rows x 2 head blocks
+    (dict(num_rows=32, max_seq_len=8192, block_table_stride=128), 4, 512),
     (dict(num_rows=256, max_seq_len=32768, block_table_stride=512), 1, 2048),
-    (dict(num_rows=256, max_seq_len=32768, block_table_stride=512, layout=2), 2, 1024),
+    (dict(num_rows=256, max_seq_len=32768, block_table_stride=512, layout=2), 1, 2048),
     (dict(num_rows=2, num_q_heads=4, kv_lora_rank=64, block_size=16,
           sel_width=32, block_table_stride=16, max_seq_len=173), 1, 64),
     (dict(chunk_tokens=192), 11, 192),
@@ -120,27 +120,26 @@ def test_split_plan(native, kw, chunks, ct):
     assert info["chunks_per_row"] == chunks
     assert info["chunk_tokens"] == ct
     assert info["merges_chunks"] == (chunks > 1)
-    assert info["workgroups"] == info["chunks_per_row"] * info["head_blocks"] * (kw.get("num_rows", 128))
-    d = kw.get("kv_lora_rank", 512)
-    paired = kw.get("layout", 0) == 2
-    assert info["layout"] == (2 if paired else 1)
-    assert info["heads_per_block"] == (32 if paired else 64)
+    rows = kw.get("num_rows", 128)
+    # (row, chunk) pairs padded to a multiple of 8, times the head blocks
+    assert info["workgroups"] == (rows * chunks + 7) // 8 * 8 * info["head_blocks"]
+    heads = kw.get("num_q_heads", 64)
+    small = kw.get("layout", 0) == 2 or heads <= 16
+    assert info["layout"] == (2 if small else 1)
+    assert info["heads_per_block"] == (16 if small else 32)
+    assert info["head_blocks"] == (heads + info["heads_per_block"] - 1) // info["heads_per_block"]
     assert info["device"] == -1
 
 
 def test_layouts(native):
-    wide = plan(native, layout=1).info()
-    paired = plan(native, layout=2).info()
-    assert (wide["heads_per_block"], wide["head_blocks"], wide["workgroups"]) == (64, 1, 256)
-    assert (paired["heads_per_block"], paired["head_blocks"], paired["workgroups"]) == (32, 2, 512)
-    assert paired["chunk_tokens"] <= 1024
-    # the planner picks the wide layout by itself; a forced chunk above the
-    # paired capacity is an error when the paired layout is asked for
+    h32 = plan(native, layout=1).info()
+    h16 = plan(native, layout=2).info()
+    assert (h32["heads_per_block"], h32["head_blocks"], h32["workgroups"]) == (32, 2, 256)
+    assert (h16["heads_per_block"], h16["head_blocks"], h16["workgroups"]) == (16, 4, 512)
+    # the planner picks 32-head blocks unless the heads fit one 16-head group
     assert plan(native).info()["layout"] == 1
-    assert plan(native, chunk_tokens=2048).info()["layout"] == 1
-    with pytest.raises(native.DsaDecodeError) as e:
-        plan(native, chunk_tokens=2048, layout=2)
-    assert "paired" in str(e.value)
+    assert plan(native, num_q_heads=16).info()["layout"] == 2
+    assert plan(native, num_q_heads=17).info()["layout"] == 1
     with pytest.raises(native.DsaDecodeError) as e:
         plan(native, layout=3)
     assert e.value.status == native.DSA_DECODE_ERR_INVALID
@@ -149,38 +148,38 @@ def test_layouts(native):
 def test_chunk_lead(native):
     # split rows: chunk 0 takes one more 128-token tile so that it finishes
     # last and merges; a forced split keeps equal chunks
-    assert plan(native).info()["chunk_lead"] == 128
-    assert plan(native, layout=2).info()["chunk_lead"] == 0   # paired: chunk 0 is at capacity
+    assert plan(native).info()["chunk_lead"] == 0          # one chunk per row
     assert plan(native, chunk_tokens=192).info()["chunk_lead"] == 0
-    one = plan(native, num_rows=256, max_seq_len=32768, block_table_stride=512, layout=1).info()
-    assert one["chunks_per_row"] == 1 and one["chunk_lead"] == 0
-    tiny = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128).info()
-    assert tiny["chunk_tokens"] == 256 and tiny["chunk_lead"] == 128
+    split = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128).info()
+    assert split["chunk_tokens"] == 512 and split["chunk_lead"] == 128
+    small = plan(native, num_rows=8, max_seq_len=8192, block_table_stride=128).info()
+    assert small["chunks_per_row"] == 16 and small["chunk_tokens"] == 128
+    assert small["chunk_lead"] == 0                         # a lead must be below the chunk
     # the ranges still cover every rank a row can have
-    for info in (plan(native).info(), plan(native, layout=2).info(), tiny):
+    for info in (plan(native).info(), split, small):
         assert info["chunks_per_row"] * info["chunk_tokens"] + info["chunk_lead"] >= 2048
-        cap = 1024 if info["layout"] == 2 else 2048
-        assert info["chunk_tokens"] + info["chunk_lead"] <= cap
+        assert info["chunk_tokens"] + info["chunk_lead"] <= 2048
 
 
 def test_workspace_layout(native):
-    p = plan(native)
-    R, W, C, H, D, HB = 128, 2048, 2, 64, 512, 1
-    need = (R * W * 4 + R * W * 8 + R * 4 + 2 * R * HB * 4 + R * C * H * D * 4
-            + R * C * H * 2 * 4)
+    p = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128)
+    R, W, C, HB, HPB, D = 32, 2048, 4, 2, 32, 512
+    need = (R * W * 4 + R * W * 8 + R * 4 + 2 * R * HB * 4 + R * HB * C * HPB * D * 4
+            + R * HB * C * HPB * 2 * 4)
     assert need <= p.workspace_bytes <= need + 6 * 256
-    p1 = plan(native, num_rows=256, max_seq_len=32768, block_table_stride=512, layout=1)
-    assert p1.info()["chunks_per_row"] == 1
-    assert p1.workspace_bytes <= 256 * 2048 * 12 + 256 * 12 + 4 * 256
+    p1 = plan(native)
+    assert p1.info()["chunks_per_row"] == 1        # no partials
+    assert p1.workspace_bytes <= 128 * 2048 * 12 + 128 * 12 + 4 * 256
 
 
 def test_head_blocks(native):
-    assert plan(native, num_q_heads=64, layout=1).info()["head_blocks"] == 1
-    assert plan(native, num_q_heads=65, layout=1).info()["head_blocks"] == 2
-    assert plan(native, num_q_heads=128, layout=1).info()["head_blocks"] == 2
-    assert plan(native, num_q_heads=64, layout=2).info()["head_blocks"] == 2
-    assert plan(native, num_q_heads=40, layout=2).info()["head_blocks"] == 2
-    assert plan(native, num_q_heads=16, layout=2).info()["head_blocks"] == 1
+    assert plan(native, num_q_heads=64, layout=1).info()["head_blocks"] == 2
+    assert plan(native, num_q_heads=65, layout=1).info()["head_blocks"] == 3
+    assert plan(native, num_q_heads=128, layout=1).info()["head_blocks"] == 4
+    assert plan(native, num_q_heads=64, layout=2).info()["head_blocks"] == 4
+    assert plan(native, num_q_heads=40, layout=2).info()["head_blocks"] == 3
+    assert plan(native, num_q_heads=16).info()["head_blocks"] == 1
+    assert plan(native, num_q_heads=8).info()["heads_per_block"] == 16
 
 
 def test_host_only_plan_cannot_launch(native):

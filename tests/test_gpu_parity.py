@@ -147,9 +147,8 @@ def test_random_shapes(H, case):
 
 @pytest.mark.parametrize("layout", [1, 2])
 def test_both_layouts_match_the_oracle(H, layout):
-    """The wide layout (64-head blocks, double-buffered tile) and the paired
-    one (32-head blocks, single-buffered, two workgroups per CU) compute the
-    same decode; run each on a split, multi-block shape."""
+    """32-head blocks (eight waves) and 16-head blocks (four waves) compute
+    the same decode; run each on a split, multi-block shape."""
     rng = np.random.default_rng(40 + layout)
     wl = WL.random_case(rng, rows=5, heads=96, D=512, block_size=64, max_len=4000,
                         width=1800)
@@ -308,6 +307,33 @@ def test_two_window_selection_beyond_262144_positions(H):
                      block_tables=bt, seq_lens=np.array([L, 400_000], np.int32), sel=sel,
                      pool=pool)
     _announce("two windows", L=L)
+    run = H.run_gpu(wl)
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, [0, 1])
+    assert H.normwise_err(run.out, want).max() <= H.TOL
+
+
+@pytest.mark.parametrize("D,B,L", [(512, 16, 300_000), (64, 16, 100_000)])
+def test_block_table_beyond_the_lds_copy(H, D, B, L):
+    """Rows whose block-table row is longer than the part the kernel copies
+    into LDS (16384 entries at D = 512, 2048 at D = 64): pages past it are
+    read from global memory. The D = 64 row also spans several bitmap
+    windows (32768 positions each)."""
+    rng = np.random.default_rng(17 + D)
+    n_pages = 64
+    per_row = -(-L // B)
+    bt = rng.integers(0, n_pages, size=(2, per_row)).astype(np.int32)
+    sel = rng.integers(-5, L + 50, size=(2, 1500)).astype(np.int32)
+    sel[:, :300] = rng.integers(L - 40_000, L, size=(2, 300))   # pages past the copy
+    pool = WL.host_pool(rng, n_pages, B, D, 1.0, 0.02)
+    wl = WL.Workload(name="bt_tail", rows=2, heads=24, D=D, block_size=B, kpool=4,
+                     width=1500, bt_stride=per_row, cache_stride_bytes=B * D,
+                     max_seq_len=L, num_pages=n_pages, sm_scale=1 / 16, k_scale=0.02,
+                     v_scale=0.02, sigma=1.0, seed=0,
+                     q_bits=WL.bf16_bits_from_f32(rng.standard_normal((2, 24, D), dtype=np.float32)),
+                     block_tables=bt, seq_lens=np.array([L, L - 7], np.int32), sel=sel,
+                     pool=pool)
+    _announce("block table tail", D=D, B=B, L=L)
     run = H.run_gpu(wl)
     H.check_selection(wl, run)
     want = H.oracle_rows(wl, [0, 1])
