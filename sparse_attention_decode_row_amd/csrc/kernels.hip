@@ -62,7 +62,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 #define DSA_LDS __attribute__((address_space(3)))
 
 constexpr int kWave = 64;
-constexpr int kTile = 128;  // tokens per staged tile (one PV operand's k extent)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // How far (log2 domain) a score may exceed the per-head reference before the
@@ -249,42 +248,44 @@ struct DecodeArgs {
   float v_scale;
 };
 
-// Waves per 16-head group: in the scoring step each takes a quarter (32
-// tokens) of the 128-token tile, so that the four quarters' weights are the
-// four exponent blocks of one PV operand.
-constexpr int kParts = 4;
+// Waves of a workgroup: per 16-head group two scoring waves, each taking
+// 32 tokens of a 64-token tile (QK^T and the softmax weights), and as many
+// PV waves, which split the latent columns between them and accumulate
+// every head group. Scoring wave w and PV wave w + kWaves/2 share a SIMD,
+// so the vector work of one runs under the matrix work of the other.
+constexpr int kTile = 64;     // tokens per staged tile
+constexpr int kBuffers = 4;   // tile buffers: two in use, two in flight
+constexpr int kParts = 2;     // scoring waves per head group (32 tokens each)
 
-// kGroups: 16-head groups per workgroup (1 or 2), kParts waves per group.
-// kSplitV: V is read from its own buffer (K and V tiles side by side,
-// single-buffered: K of the next tile loads during PV, V during QK).
-// Otherwise K and V are the same bytes and two tile buffers alternate: the
-// next tile loads while one is consumed.
+// kGroups: 16-head groups per workgroup (1 or 2).
+// kSplitV: V is read from its own buffer (two K and two V tile buffers;
+// the next tile's K and this tile's V load while the current ones are
+// consumed). Otherwise K and V are the same bytes, in four tile buffers:
+// tile i is scored while tile i-1 is accumulated and tiles i+1, i+2 load.
 template <int D, int kGroups, bool kSplitV>
-__global__ __launch_bounds__(kParts * kGroups * kWave, 1)
+__global__ __launch_bounds__(4 * kGroups * kWave, 1)
 void dsa_decode_kernel(DecodeArgs a) {
-  constexpr int kWaves = kParts * kGroups;
+  constexpr int kQKWaves = kParts * kGroups;
+  constexpr int kPVWaves = kQKWaves;
+  constexpr int kWaves = kQKWaves + kPVWaves;
   constexpr int kThreads = kWave * kWaves;
   constexpr int kTileBytes = kTile * D;
-  constexpr int kSmemBytes = 2 * kTileBytes;
+  constexpr int kSmemBytes = kBuffers * kTileBytes;
   constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
-  // PV: a wave accumulates kPair head groups over kCB column blocks, so each
-  // V operand read feeds 2*kPair MFMAs.
-  constexpr int kPair = (kGroups == 2 && kDBlocks >= kWaves) ? 2 : 1;
-  constexpr int kPairs = kGroups / kPair;           // PV head sets
-  constexpr int kCB = kPairs * kDBlocks / kWaves;   // column blocks per PV wave
+  constexpr int kCB = kDBlocks / kPVWaves;          // column blocks per PV wave (all groups)
   constexpr int kChunkMask = (kDBlocks < 16 ? kDBlocks : 16) - 1;
-  // Gather: a latent row is D/16 lanes of 16 bytes.
+  // Gather: a latent row is D/16 lanes of 16 bytes; the PV waves move the tiles.
   constexpr int kLanesPerTok = D / 16;
   constexpr int kTokPerInstr = kWave / kLanesPerTok;
-  constexpr int kTPW = kTile / kWaves;              // tokens each wave DMAs per tile
-  constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per wave per tile
+  constexpr int kTPW = kTile / kPVWaves;            // tokens each PV wave DMAs per tile
+  constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per PV wave per tile
   // Selection: before the first tile the tile buffers hold the membership
   // bitmap of a window of positions (a quarter), each word's rank (a
   // quarter) and the row's block-table entries (the upper half).
   constexpr int kWinWords = kSmemBytes / 16;
   constexpr int kBtCap = kSmemBytes / 8;
-  static_assert(kCB >= 1 && kPairs * kDBlocks == kCB * kWaves, "PV column split");
+  static_assert(kCB >= 1 && kCB * kPVWaves == kDBlocks, "PV column split");
   static_assert(kInstr >= 1 && kInstr * kTokPerInstr == kTPW, "DMA split");
   static_assert(kBtCap % kWave == 0 && kWinWords % 4 == 0, "selection areas");
   static_assert(16 * D + 256 * ((kKSteps - 1) >> 1) < 65536,
@@ -292,20 +293,23 @@ void dsa_decode_kernel(DecodeArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
-  // softmax weights of a tile, [group][quarter][hi|lo][head][lane group] x 8 bytes
-  __shared__ __attribute__((aligned(16))) i32x2 xch_p[kGroups][kParts][2][16][4];
-  __shared__ int xch_e[kGroups][kParts][16];  // their E8M0 exponent bytes, per head
-  __shared__ float xch_f[kWaves][kWave];      // per-head scalars between the waves of a group
-  __shared__ float xch_m[kGroups][kWave];     // per-head reference, for the PV waves
+  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kMaxChunkTokens];
+  // softmax weights of a tile as PV B operands: [tile parity][group][hi|lo][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) i32x4 xch_p[2][kGroups][2][kWave];
+  __shared__ int xch_e[2][kGroups][kParts][16];  // their E8M0 exponent bytes, per head
+  __shared__ float xch_f[kWaves][kWave];         // per-head scalars between waves
+  __shared__ float xch_m[kGroups][kWave];        // per-head reference, for the PV waves
   __shared__ int scan_sh[kWaves];
   __shared__ int flag_sh;
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: role branches are scalar
   const int g = lane >> 4, li = lane & 15;
-  // QK role: head group hg, tile quarter `part`. PV role: head groups
-  // pset*kPair + x (x < kPair), column blocks jbase .. jbase + kCB - 1.
-  const int hg = wave % kGroups, part = wave / kGroups;
-  const int pset = wave % kPairs, jbase = (wave / kPairs) * kCB;
+  const bool is_qk = wave < kQKWaves;
+  // Scoring role: head group hg, tile half `part` (tokens 32*part .. +31).
+  const int hg = wave % kGroups, part = (wave % kQKWaves) / kGroups;
+  // PV role: every head group, column blocks jbase .. jbase + kCB - 1.
+  const int pw = wave - kQKWaves, jbase = (wave % kPVWaves) * kCB;
 
   // Workgroup -> (row, chunk, head block). The head blocks of one (row,
   // chunk) read the same latent rows, so they get ids 8 apart: the same XCD
@@ -317,8 +321,6 @@ void dsa_decode_kernel(DecodeArgs a) {
   if (rc >= a.rows * a.chunks) return;  // grid padding
   const int r = rc / a.chunks, c = rc % a.chunks;
 
-  const int head = hb * a.heads_per_block + hg * 16 + li;
-  const bool head_ok = head < a.H;
   DSA_LDS uint8_t* lds = (DSA_LDS uint8_t*)smem;
 
   // ------------------------------------------------------------ 1. selection
@@ -346,19 +348,23 @@ void dsa_decode_kernel(DecodeArgs a) {
     dma4(bt + min(i * kWave + lane, nbt - 1), (DSA_LDS void*)(lds + kSmemBytes / 2 + i * 4 * kWave));
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
 
-  // This wave's share of the query: head li, latent columns 128*ks + 32*g +
-  // [0, 32). With several k-steps the four waves of a group take k-steps
-  // ks = 4*i + part and exchange the FP8 terms through tile buffer memory
-  // not yet in use (4 KiB per group and k-step); a single k-step is loaded
-  // by every wave.
+  // The query as FP8 terms is prepared by all waves: wave w converts head
+  // group w % kGroups, k-steps ks = 4*i + w / kGroups, and the terms are
+  // exchanged through tile buffers 2 and 3 (4 KiB per group and k-step). A
+  // single k-step is loaded by every wave.
+  constexpr int kQWaysPerGroup = kWaves / kGroups;  // 4
+  const int qsub = wave / kGroups;
+  const int q_head = hb * a.heads_per_block + hg * 16 + li;
+  const bool q_ok = q_head < a.H;
   constexpr bool kShareQ = kKSteps >= 2;
-  constexpr int kKOwn = kShareQ ? (kKSteps + kParts - 1) / kParts : kKSteps;
-  static_assert(!kShareQ || kGroups * kKSteps * 4096 <= kTileBytes, "query exchange area");
-  auto own_ks = [&](int i) { return kShareQ ? kParts * i + part : i; };
+  constexpr int kKOwn = kShareQ ? (kKSteps + kQWaysPerGroup - 1) / kQWaysPerGroup : kKSteps;
+  constexpr int kQxOff = 2 * kTileBytes;
+  static_assert(!kShareQ || kGroups * kKSteps * 4096 <= 2 * kTileBytes, "query exchange area");
+  auto own_ks = [&](int i) { return kShareQ ? kQWaysPerGroup * i + qsub : i; };
   u32x4 qraw[kKOwn][4];
   auto load_q = [&]() {
     wait_vmcnt<0>();  // the block-table DMA (issued before) has landed
-    const uint16_t* qrow = a.q + ((size_t)r * a.H + (head_ok ? head : 0)) * D;
+    const uint16_t* qrow = a.q + ((size_t)r * a.H + (q_ok ? q_head : 0)) * D;
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
       const int ks = min(own_ks(i), kKSteps - 1);
@@ -448,15 +454,12 @@ void dsa_decode_kernel(DecodeArgs a) {
   if (!q_loaded) load_q();
   const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
+  const bool exporter = hb == 0;  // exports the ids and offsets of the row (after the loop)
 
   // ids -> latent row indices (page * rows per page + slot in page) through
   // the block-table entries in LDS (global memory for a page beyond them).
-  // The head-block-0 workgroups of the row export the ids and byte offsets.
   {
     const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
-    const bool exporter = hb == 0;
-    int32_t* idw = a.ws_ids + (size_t)r * a.width + cstart;
-    uint64_t* offw = a.ws_offsets + (size_t)r * a.width + cstart;
     for (int i0 = tid; i0 < n; i0 += 4 * kThreads) {
       int t[4];
       uint32_t page[4];
@@ -473,26 +476,20 @@ void dsa_decode_kernel(DecodeArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * kThreads;
         if (i < n) {
-          const uint32_t row = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
-          rows_lds[i] = row;
-          if (exporter) {
-            idw[i] = t[u];
-            offw[i] = (uint64_t)row * (uint64_t)D;
-          }
+          rows_lds[i] = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
+          if (exporter) ids_lds[i] = t[u];
         }
       }
     }
-    if (c == 0 && hb == 0 && tid == 0) a.ws_counts[r] = total;
   }
 
   // ---- the query as two FP8 terms under a per-head power-of-two scale that
   // puts the head's largest |q| in [128, 256)
-  i32x8 qhi[kKSteps], qlo[kKSteps];
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < kKOwn; ++i) {
     const int ks = own_ks(i);
-    if (!head_ok || ks >= kKSteps || 128 * ks + 32 * g >= D)
+    if (!q_ok || ks >= kKSteps || 128 * ks + 32 * g >= D)
 #pragma unroll
       for (int v = 0; v < 4; ++v) qraw[i][v] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -503,21 +500,22 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
   amax = max_xor32(max_xor16(amax));
   if constexpr (kShareQ) xch_f[wave][lane] = amax;
-  __syncthreads();  // row table written (block-table area free); the groups' maxima visible
+  __syncthreads();  // row table written (selection areas free); the groups' maxima visible
   // pad to whole tiles with the last real row (loaded, weighted by zero)
   if (n > 0)
     for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
   float score_scale;
+  i32x8 qhi[kKSteps], qlo[kKSteps];
   {
     if constexpr (kShareQ)
 #pragma unroll
-      for (int p = 0; p < kParts; ++p) amax = fmaxf(amax, xch_f[hg + kGroups * p][lane]);
+      for (int p = 0; p < kQWaysPerGroup; ++p) amax = fmaxf(amax, xch_f[hg + kGroups * p][lane]);
     const int e = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xff) - 127 : 0;
     int sh = 7 - e;
     sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
     const float qs = pow2i(sh);
-    // exchange area in the second tile buffer: [group][ks][hi|lo][half][lane]
-    u32x4* qx = (u32x4*)(smem + kTileBytes);
+    // exchange area: [group][ks][hi|lo][half][lane]
+    u32x4* qx = (u32x4*)(smem + kQxOff);
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
       const int ks = own_ks(i);
@@ -552,52 +550,72 @@ void dsa_decode_kernel(DecodeArgs a) {
   __syncthreads();  // row table padded; the groups' FP8 terms visible
 
   // -------------------------------------------------------------- 2. gather
-  // Wave w moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its instruction k
+  // PV wave p moves tokens [p*kTPW, (p+1)*kTPW) of a tile. Its instruction k
   // writes kTokPerInstr consecutive LDS slots; DMA lane l carries chunk
-  // l % kLanesPerTok of token w*kTPW + (l / kLanesPerTok)*kInstr + k, so a
+  // l % kLanesPerTok of token p*kTPW + (l / kLanesPerTok)*kInstr + k, so a
   // lane's kInstr row indices are contiguous in the row table.
   const DSA_LDS uint32_t* rows_l = (const DSA_LDS uint32_t*)rows_lds;
-  auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
-    const int j = lane / kLanesPerTok, ci = lane % kLanesPerTok;
-    const DSA_LDS uint32_t* rr = rows_l + tile * kTile + wave * kTPW + j * kInstr;
-    uint32_t row[kInstr];
+  const int pw_s = wave % kPVWaves;
+  auto tile_rows = [&](int tile, uint32_t (&row)[kInstr]) {
+    const DSA_LDS uint32_t* rr =
+        rows_l + tile * kTile + pw_s * kTPW + (lane / kLanesPerTok) * kInstr;
 #pragma unroll
     for (int k = 0; k < kInstr; ++k) row[k] = rr[k];
+  };
+  // Lane l carries chunk ci of token slot0 + j. slot0 is a multiple of
+  // kTokPerInstr (a power of two) and j < kTokPerInstr, so the token's
+  // swizzle is the uniform swizzle of slot0 XOR j: one per-lane constant.
+  const uint32_t dma_c0 =
+      (uint32_t)(((lane % kLanesPerTok) ^ ((lane / kLanesPerTok) & kChunkMask)) << 4);
+  auto dma_one = [&](int k, uint32_t row, int dst_off, const uint8_t* src,
+                     uint32_t c0) {
+    const int slot0 = pw_s * kTPW + k * kTokPerInstr;
+    const uint32_t chunk = c0 ^ ((uint32_t)tile_swizzle<D>(slot0) << 4);  // < D
+    const uint64_t off = (uint64_t)row * (uint64_t)D | (uint64_t)chunk;
+    dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
+  };
+  auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
+    uint32_t row[kInstr];
+    tile_rows(tile, row);
 #pragma unroll
-    for (int k = 0; k < kInstr; ++k) {
-      const int slot0 = wave * kTPW + k * kTokPerInstr;
-      const int swz = tile_swizzle<D>(slot0 + j);
-      const uint64_t off = (uint64_t)row[k] * (uint64_t)D + (uint64_t)((ci ^ swz) << 4);
-      dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
-    }
+    for (int k = 0; k < kInstr; ++k) dma_one(k, row[k], dst_off, src, dma_c0);
   };
   // Token index (within the tile) held by LDS slot s.
   auto token_of_slot = [&](int s) {
     const int w = s / kTPW, sw = s % kTPW;
     return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
   };
-  // Tile 0's K (and, when K and V are the same bytes, its V) goes out now;
-  // a separate V buffer is filled at the top of the first tile, after every
-  // wave has read its query terms out of it.
-  if (ntiles > 0) issue_tile(0, 0, a.k_cache);
-
+  // LDS byte offsets of the buffers holding tile i's K and V.
+  auto k_off = [&](int i) { return kSplitV ? (i & 1) * kTileBytes : (i & 3) * kTileBytes; };
+  auto v_off = [&](int i) { return kSplitV ? (2 + (i & 1)) * kTileBytes : (i & 3) * kTileBytes; };
+  // The first tiles (tile 0; with K and V the same bytes also tile 1) go out
+  // now; a separate V buffer is filled in the loop after every wave has read
+  // its query terms out of it.
+  auto issue_first = [&]() {
+    if (!is_qk) {
+      if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
+      if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
+    }
+  };
   if constexpr (kShareQ) {
-    const u32x4* qx = (const u32x4*)(smem + kTileBytes);
+    if (is_qk) {
+      const u32x4* qx = (const u32x4*)(smem + kQxOff);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
-      const u32x4 h1 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 1) * kWave + lane];
-      const u32x4 l0 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 0) * kWave + lane];
-      const u32x4 l1 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 1) * kWave + lane];
-      qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
-      qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
+        const u32x4 h1 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 1) * kWave + lane];
+        const u32x4 l0 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 0) * kWave + lane];
+        const u32x4 l1 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 1) * kWave + lane];
+        qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      }
     }
   }
 
-  // K operand addresses. This wave scores blocks b = 2*part + k (k < 2) of
-  // 16 slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk position
-  // (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position is
-  // 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ k) & 1)), so four per-lane
+  // K operand addresses of a scoring wave. It scores blocks b = 2*part + k
+  // (k < 2) of 16 slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk
+  // position (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position
+  // is 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ k) & 1)), so four per-lane
   // offsets plus compile-time immediates cover every read.
   int kofs[2][2];
 #pragma unroll
@@ -606,235 +624,298 @@ void dsa_decode_kernel(DecodeArgs a) {
     for (int h = 0; h < 2; ++h)
       kofs[p][h] = 32 * D * part + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
 
-  // V operand rows. Operand bytes 8u .. 8u+7 of lane group g come from the
-  // scoring lanes of group g' = 2*(g & 1) + (u & 1) in quarter
-  // P = 2*(u >> 1) + (g >> 1): byte i is slot 32*P + 16*(i >> 2) + 4*g' +
-  // (i & 3). A transposing read hands lane li the 8 bytes of its column from
-  // 8 rows; lanes 2k and 2k+1 of the 16-lane group supply row k (column
-  // halves 0 and 1).
-  int vrow[4], vswz[4];
+  // PV operands. B (the weights, per head): lane group g holds the 16
+  // tokens T_g of tile half g >> 1 that scoring lane groups (g & 1) and
+  // (g & 1) + 2 of that half score, as bytes 0-15 (hi terms) and 16-31 (lo
+  // terms). The operand's four exponent blocks are then {hi, lo} x {half 0,
+  // half 1}: each the weights of one scoring wave for the head. A (V): lane
+  // group g needs the same 16 tokens' latent column in bytes 0-15 and again
+  // in 16-31. Byte i of the 8 supplied by scoring lane group g' of half P is
+  // slot 32*P + 16*(i >> 2) + 4*g' + (i & 3). A transposing read hands lane
+  // li the 8 bytes of its column from 8 rows; lanes 2k and 2k+1 of the
+  // 16-lane group supply row k (column halves 0 and 1). (Lane groups 0 and
+  // 1, read together, cover distinct swizzled chunk positions, as do 2 and
+  // 3.)
+  int vrow[2], vswz[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int P = 2 * (u >> 1) + (g >> 1), gp = 2 * (g & 1) + (u & 1), rr = li >> 1;
+  for (int u = 0; u < 2; ++u) {
+    const int P = g >> 1, gp = (g & 1) + 2 * u, rr = li >> 1;
     const int slot = 32 * P + 16 * (rr >> 2) + 4 * gp + (rr & 3);
     vrow[u] = slot * D + 8 * (li & 1);
     vswz[u] = tile_swizzle<D>(slot) << 4;
   }
 
   // -------------------------------------------------------------- 3. attend
-  // The accumulators are touched only by the matrix cores inside the tile
-  // loop: weights are taken against a fixed per-head reference (the first
-  // tile's max), and each quarter's 32 weights of a head carry their own
-  // E8M0 exponent, so a later score may exceed the reference by up to
-  // 2^kSlack without leaving the FP8 range or fp32 accumulation. Should a
-  // score ever exceed it by more (only with pathological inputs), the chunk
-  // is recomputed with the reference set to the exact maximum seen.
-  f32x4 O[kPair][kCB];
-  float l_part = 0.f;        // this wave's share of sum_t 2^(s_t - m_ref), per head
+  // Step i scores tile i (scoring waves) and accumulates tile i - 1 (PV
+  // waves), between one barrier and the next. The accumulators are touched
+  // only by the matrix cores: weights are taken against a fixed per-head
+  // reference (the first tile's max), and each scoring wave's 32 weights of
+  // a head carry their own E8M0 exponent, so a later score may exceed the
+  // reference by up to 2^kSlack without leaving the FP8 range or fp32
+  // accumulation. Should a score ever exceed it by more (only with
+  // pathological inputs), the chunk is recomputed with the reference set to
+  // the exact maximum seen.
+  f32x4 O[kGroups][kCB];
+  float l_part = 0.f;        // this scoring wave's share of sum_t 2^(s_t - m_ref), per head
   float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
   float m_seen = -INFINITY;  // exact max of this wave's scores so far
-
-  for (int pass = 0; pass < 2; ++pass) {
+  // After the first pass: recompute the chunk only if some scoring wave saw
+  // a score beyond the slack (every wave takes part; two barriers).
+  auto redo_needed = [&](bool overflow) {
+    if (__any(overflow) && lane == 0) flag_sh = 1;
+    xch_f[wave][lane] = m_seen;
+    __syncthreads();
+    const bool redo = flag_sh != 0;
+    if (redo && is_qk) {
+      float m = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < kPair; ++x)
-#pragma unroll
-      for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    l_part = 0.f;
-    bool overflow = false;
-    if (pass == 1 && ntiles > 0) issue_tile(0, 0, a.k_cache);
-
-    for (int it = 0; it < ntiles; ++it) {
-      wait_vmcnt<0>();
-      barrier_lds();  // tile `it` (its K half when split) is in LDS; PV of it-1 is done
-      int koff, voff;
-      if constexpr (kSplitV) {
-        koff = 0;
-        voff = kTileBytes;
-        issue_tile(it, kTileBytes, a.v_cache);  // the V buffer is free again
-      } else {
-        koff = voff = (it & 1) * kTileBytes;
-        if (it + 1 < ntiles) issue_tile(it + 1, ((it + 1) & 1) * kTileBytes, a.k_cache);
-      }
-
-      // ---- S^T = K Q^T over this wave's two blocks, K operands prefetched
-      // kKPre MFMA steps ahead
-      const DSA_LDS uint8_t* kt = lds + koff;
-      constexpr int kSteps = 2 * kKSteps;
-      auto load_k = [&](int s) -> i32x8 {
-        const int k = s / kKSteps, ks = s % kKSteps;
-        i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (128 * ks + 32 * g < D) {
-          const int p = (ks ^ k) & 1;
-          const DSA_LDS uint8_t* base = kt + 16 * k * D + 256 * (ks >> 1);
-          const u32x4 lo = *(const DSA_LDS u32x4*)(base + kofs[p][0]);
-          const u32x4 hi = *(const DSA_LDS u32x4*)(base + kofs[p][1]);
-          kop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        }
-        return kop;
-      };
-      f32x4 S[2];
-      constexpr int kKPre = 3;
-      i32x8 kbuf[kKPre + 1];
-#pragma unroll
-      for (int s = 0; s < kKPre && s < kSteps; ++s) kbuf[s] = load_k(s);
-#pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const int k = s / kKSteps, ks = s % kKSteps;
-        if (s + kKPre < kSteps) kbuf[(s + kKPre) % (kKPre + 1)] = load_k(s + kKPre);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qhi[ks], S[k]);
-        S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qlo[ks], S[k]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // ---- weights. The lane holds head li at slots 32*part + 16*k + 4*g +
-      // i; the wave's 32 weights of a head share one FP8 exponent.
-      const int nvalid = n - it * kTile;
-      if (__builtin_expect(nvalid < kTile, 0)) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
-      }
-      float mh = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        mh = fmaxf(mh, fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3])));
-      mh = max_xor32(max_xor16(mh)) * score_scale;  // score_scale > 0
-      m_seen = fmaxf(m_seen, mh);
-      if (pass == 0 && it == 0) {
-        // first tile: the reference is the tile's max over the group's four
-        // quarters (a workgroup-uniform branch: it holds a barrier)
-        xch_f[wave][lane] = mh;
-        barrier_lds();
-        float m = mh;
-#pragma unroll
-        for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
-        m_ref = m;
-      }
-      overflow |= mh > m_ref + kSlack;
-      const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
-      // quarter exponent: the quarter's largest weight maps to [128, 256)
-      int e = mh == -INFINITY ? 0 : (int)floorf(mh - mbase);
-      e = e < -100 ? -100 : (e > 100 ? 100 : e);
-      const float bsub = mbase + (float)(e - 7);
-      i32x2 phi, plo;
-      float lsum = 0.f;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
-        lsum += (p[0] + p[1]) + (p[2] + p[3]);
-        int hi, lo;
-        split_fp8x4(p[0], p[1], p[2], p[3], hi, lo);
-        phi[k] = hi;
-        plo[k] = lo;
-      }
-      l_part += lsum * pow2i(e - 7);
-      xch_p[hg][part][0][li][g] = phi;
-      xch_p[hg][part][1][li][g] = plo;
-      if (g == 0) xch_e[hg][part][li] = e + 120;
-
-      if constexpr (kSplitV) {
-        wait_vmcnt<0>();  // V of this tile
-        barrier_lds();    // every wave's V rows landed, K reads done, weights visible
-        if (it + 1 < ntiles) issue_tile(it + 1, 0, a.k_cache);
-      } else {
-        barrier_lds();    // weights visible (the next tile stays in flight)
-      }
-
-      // ---- full P^T operands of this wave's head groups: bytes 0-15 of lane
-      // group g from quarter g >> 1, bytes 16-31 from quarter 2 + (g >> 1),
-      // each 8 bytes of scoring lane groups 2*(g & 1) and 2*(g & 1) + 1; lane
-      // group g's scale byte is quarter g's exponent (the operand block it
-      // scales)
-      i32x8 pH[kPair], pL[kPair];
-      int psc[kPair];
-#pragma unroll
-      for (int x = 0; x < kPair; ++x) {
-        const int hx = pset * kPair + x;
-        const i32x4 h0 = *(const i32x4*)&xch_p[hx][g >> 1][0][li][2 * (g & 1)];
-        const i32x4 h1 = *(const i32x4*)&xch_p[hx][2 + (g >> 1)][0][li][2 * (g & 1)];
-        const i32x4 l0 = *(const i32x4*)&xch_p[hx][g >> 1][1][li][2 * (g & 1)];
-        const i32x4 l1 = *(const i32x4*)&xch_p[hx][2 + (g >> 1)][1][li][2 * (g & 1)];
-        pH[x] = i32x8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        pL[x] = i32x8{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-        psc[x] = xch_e[hx][g][li];
-      }
-
-      // ---- O^T += V^T P^T over this wave's column blocks (one 128-token
-      // operand per MFMA, shared by the head groups), V operands of the next
-      // blocks prefetched.
-      const DSA_LDS uint8_t* vt = lds + voff;
-      auto load_v = [&](int j0) -> i32x8 {
-        i32x8 vop;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int addr = (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
-          const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
-          vop[2 * u] = v2.x;
-          vop[2 * u + 1] = v2.y;
-        }
-        return vop;
-      };
-      constexpr int kVPre = 2;
-      i32x8 vbuf[kVPre + 1];
-#pragma unroll
-      for (int j = 0; j < kVPre && j < kCB; ++j) vbuf[j] = load_v(j);
-#pragma unroll
-      for (int j0 = 0; j0 < kCB; ++j0) {
-        if (j0 + kVPre < kCB) vbuf[(j0 + kVPre) % (kVPre + 1)] = load_v(j0 + kVPre);
-        __builtin_amdgcn_sched_barrier(0);
-        const i32x8& vop = vbuf[j0 % (kVPre + 1)];
-#pragma unroll
-        for (int x = 0; x < kPair; ++x)
-          O[x][j0] = mfma_fp8_bscaled(vop, pH[x], psc[x], O[x][j0]);
-#pragma unroll
-        for (int x = 0; x < kPair; ++x)
-          O[x][j0] = mfma_fp8_bscaled(vop, pL[x], psc[x], O[x][j0]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
+      m_ref = m;
     }
-    // Recompute the chunk only if some wave saw a score beyond the slack.
-    if (pass == 0) {
-      if (__any(overflow) && lane == 0) flag_sh = 1;
-      xch_f[wave][lane] = m_seen;
-      __syncthreads();
-      const bool redo = flag_sh != 0;
-      if (redo) {
-        float m = m_seen;
+    __syncthreads();
+    return redo;
+  };
+
+  // Both roles run the same sequence of barriers: one at the top of each
+  // step, in the first step of the first pass one more for the reference,
+  // and two after the first pass. Step i scores tile i and accumulates tile
+  // i - 1. Each role keeps its own registers (the query terms, the
+  // accumulators) inside its own branch.
+  if (is_qk) {
+    for (int pass = 0; pass < 2; ++pass) {
+      l_part = 0.f;
+      bool overflow = false;
+        for (int it = 0; it <= ntiles; ++it) {
+          // tile it's K in LDS; every read of the weights of it - 2 done
+          barrier_lds();
+          const bool score = it < ntiles;
+
+          // ---- S^T = K Q^T over this wave's two blocks, K operands
+          // prefetched kKPre MFMA steps ahead
+          f32x4 S[2];
+          float mh = -INFINITY;
+          if (score) {
+            const DSA_LDS uint8_t* kt = lds + k_off(it);
+            constexpr int kSteps = 2 * kKSteps;
+            auto load_k = [&](int s) -> i32x8 {
+              const int k = s / kKSteps, ks = s % kKSteps;
+              i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
+              if (128 * ks + 32 * g < D) {
+                const int p = (ks ^ k) & 1;
+                const DSA_LDS uint8_t* base = kt + 16 * k * D + 256 * (ks >> 1);
+                const u32x4 lo = *(const DSA_LDS u32x4*)(base + kofs[p][0]);
+                const u32x4 hi = *(const DSA_LDS u32x4*)(base + kofs[p][1]);
+                kop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+              }
+              return kop;
+            };
+            constexpr int kKPre = 3;
+            i32x8 kbuf[kKPre + 1];
+            // The scoring wave's matrix work goes first on its SIMD; the PV
+            // wave's then runs under this wave's softmax.
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-        for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
-        m_ref = m;
-      }
-      __syncthreads();
-      if (!redo) break;
+            for (int s = 0; s < kKPre && s < kSteps; ++s) kbuf[s] = load_k(s);
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) {
+              const int k = s / kKSteps, ks = s % kKSteps;
+              if (s + kKPre < kSteps) kbuf[(s + kKPre) % (kKPre + 1)] = load_k(s + kKPre);
+              __builtin_amdgcn_sched_barrier(0);
+              if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+              S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qhi[ks], S[k]);
+              S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qlo[ks], S[k]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            // The lane holds head li at slots 32*part + 16*k + 4*g + i.
+            const int nvalid = n - it * kTile;
+            if (__builtin_expect(nvalid < kTile, 0)) {
+#pragma unroll
+              for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              mh = fmaxf(mh, fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3])));
+            mh = max_xor32(max_xor16(mh)) * score_scale;  // score_scale > 0
+            m_seen = fmaxf(m_seen, mh);
+          }
+          if (pass == 0 && it == 0) {
+            // first tile: the reference is the tile's max over the group's
+            // scoring waves
+            if (score) xch_f[wave][lane] = mh;
+            barrier_lds();
+            if (ntiles > 0) {
+              float m = -INFINITY;
+#pragma unroll
+              for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
+              m_ref = m;
+            }
+          }
+          if (score) {
+            // ---- weights: the wave's largest weight of the head maps to [128, 256)
+            overflow |= mh > m_ref + kSlack;
+            const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
+            int e = mh == -INFINITY ? 0 : (int)floorf(mh - mbase);
+            e = e < -100 ? -100 : (e > 100 ? 100 : e);
+            const float bsub = mbase + (float)(e - 7);
+            i32x2 phi, plo;
+            float lsum = 0.f;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              float p[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
+              lsum += (p[0] + p[1]) + (p[2] + p[3]);
+              int hi, lo;
+              split_fp8x4(p[0], p[1], p[2], p[3], hi, lo);
+              phi[k] = hi;
+              plo[k] = lo;
+            }
+            l_part += lsum * pow2i(e - 7);
+            // this lane's 8 bytes are bytes 8*(g >> 1) .. +7 (hi terms) and
+            // 16 + 8*(g >> 1) .. (lo terms) of PV lane group 2*part + (g & 1),
+            // head li
+            const int pl = (2 * part + (g & 1)) * 16 + li;
+            ((i32x2*)&xch_p[it & 1][hg][0][pl])[g >> 1] = phi;
+            ((i32x2*)&xch_p[it & 1][hg][1][pl])[g >> 1] = plo;
+            if (g == 0) xch_e[it & 1][hg][part][li] = e + 120;
+          }
+        }
+      if (pass == 0 && !redo_needed(overflow)) break;
+    }
+  } else {
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int x = 0; x < kGroups; ++x)
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      issue_first();
+        for (int it = 0; it <= ntiles; ++it) {
+          // Tile it has landed: wait for every DMA of this wave but the next
+          // tile's, then the barrier (tile it - 1's V and weights visible,
+          // every read of tile it - 2's buffer done).
+          if (!kSplitV && it + 1 < ntiles) wait_vmcnt<kInstr>();
+          else wait_vmcnt<0>();
+          barrier_lds();
+          if (pass == 0 && it == 0) barrier_lds();  // the scoring waves' reference exchange
+
+          // ---- gather: tile it + 2 (or, with a separate V buffer, K of it +
+          // 1 and V of it), its instructions spread over the PV steps below
+          // so that the vector memory queue never stalls this wave for long.
+          // (The lane constant is laundered per step: address arithmetic is
+          // then redone each time instead of being held in registers.)
+          uint32_t c0 = dma_c0;
+          asm volatile("" : "+v"(c0));
+          constexpr int kNd = kSplitV ? 2 * kInstr : kInstr;
+          const bool dk = kSplitV ? it + 1 < ntiles : it + 2 < ntiles;
+          const bool dv = kSplitV && it < ntiles;
+          uint32_t drow[kNd];
+          if (dk) {
+            uint32_t rk[kInstr];
+            tile_rows(kSplitV ? it + 1 : it + 2, rk);
+#pragma unroll
+            for (int k = 0; k < kInstr; ++k) drow[k] = rk[k];
+          }
+          if (dv) {
+            uint32_t rv[kInstr];
+            tile_rows(it, rv);
+#pragma unroll
+            for (int k = 0; k < kInstr; ++k) drow[kNd - kInstr + k] = rv[k];
+          }
+          auto dma_step = [&](int d) {
+            if (d < kInstr) {
+              if (dk) dma_one(d, drow[d], k_off(kSplitV ? it + 1 : it + 2), a.k_cache, c0);
+            } else {
+              if (dv) dma_one(d - kInstr, drow[d], v_off(it), a.v_cache, c0);
+            }
+          };
+          if (it == 0) {
+#pragma unroll
+            for (int d = 0; d < kNd; ++d) dma_step(d);
+            continue;
+          }
+          // ---- O^T += V^T P^T for tile it - 1 over this wave's column
+          // blocks: one MFMA per head group and block (64 tokens, hi and lo
+          // terms), V operands prefetched kVPre blocks ahead.
+          const int pt = it - 1;
+          i32x8 pB[kGroups];
+          int psc[kGroups];
+#pragma unroll
+          for (int x = 0; x < kGroups; ++x) {
+            const i32x4 h = xch_p[pt & 1][x][0][lane], l = xch_p[pt & 1][x][1][lane];
+            pB[x] = i32x8{h.x, h.y, h.z, h.w, l.x, l.y, l.z, l.w};
+            psc[x] = xch_e[pt & 1][x][g & 1][li];
+          }
+          const DSA_LDS uint8_t* vt = lds + v_off(pt);
+          auto load_v = [&](int j0) -> i32x8 {
+            i32x8 vop;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int addr = (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
+              const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
+              vop[2 * u] = v2.x;
+              vop[2 * u + 1] = v2.y;
+              vop[4 + 2 * u] = v2.x;
+              vop[4 + 2 * u + 1] = v2.y;
+            }
+            return vop;
+          };
+          constexpr int kVPre = 2;
+          i32x8 vbuf[kVPre + 1];
+#pragma unroll
+          for (int j = 0; j < kVPre && j < kCB; ++j) vbuf[j] = load_v(j);
+#pragma unroll
+          for (int j0 = 0; j0 < kCB; ++j0) {
+            if (j0 + kVPre < kCB) vbuf[(j0 + kVPre) % (kVPre + 1)] = load_v(j0 + kVPre);
+#pragma unroll
+            for (int d = j0 * kNd / kCB; d < (j0 + 1) * kNd / kCB; ++d) dma_step(d);
+            __builtin_amdgcn_sched_barrier(0);
+            const i32x8& vop = vbuf[j0 % (kVPre + 1)];
+#pragma unroll
+            for (int x = 0; x < kGroups; ++x)
+              O[x][j0] = mfma_fp8_bscaled(vop, pB[x], psc[x], O[x][j0]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+          if (pass == 0 && !redo_needed(false)) break;
     }
   }
 
-  // Weight sums and references of the PV waves' heads (all four quarters).
-  xch_f[wave][lane] = sum_xor32(sum_xor16(l_part));
-  if (part == 0) xch_m[hg][lane] = ntiles > 0 ? m_ref : -INFINITY;
+  // Weight sums and references of the heads, for the PV waves.
+  if (is_qk) {
+    xch_f[wave][lane] = sum_xor32(sum_xor16(l_part));
+    if (part == 0) xch_m[hg][lane] = ntiles > 0 ? m_ref : -INFINITY;
+  }
   __syncthreads();
-  float l_run[kPair], m_run[kPair];
+  float l_run[kGroups], m_run[kGroups];
 #pragma unroll
-  for (int x = 0; x < kPair; ++x) {
-    const int hx = pset * kPair + x;
+  for (int x = 0; x < kGroups; ++x) {
     l_run[x] = 0.f;
 #pragma unroll
-    for (int p = 0; p < kParts; ++p) l_run[x] += xch_f[hx + kGroups * p][lane];
-    m_run[x] = xch_m[hx][lane];
+    for (int p = 0; p < kParts; ++p) l_run[x] += xch_f[x + kGroups * p][lane];
+    m_run[x] = xch_m[x][lane];
+  }
+
+  // The ids of the row and their byte offsets (head block 0 exports them).
+  if (exporter && is_qk) {
+    int32_t* idw = a.ws_ids + (size_t)r * a.width + cstart;
+    uint64_t* offw = a.ws_offsets + (size_t)r * a.width + cstart;
+    for (int i = tid; i < n; i += kQKWaves * kWave) {
+      idw[i] = ids_lds[i];
+      offw[i] = (uint64_t)rows_lds[i] * (uint64_t)D;
+    }
+    if (c == 0 && tid == 0) a.ws_counts[r] = total;
   }
 
   // --------------------------------------------------------------- 4. merge
-  // Lane holds O^T rows d = 16*(jbase + j) + 4*g + i for head li of group
-  // pset*kPair + x.
+  // A PV lane holds O^T rows d = 16*(jbase + j) + 4*g + i for head li of
+  // group x.
   auto store_out = [&](int x, const f32x4* o, float lsum) {
-    const int hx = hb * a.heads_per_block + (pset * kPair + x) * 16 + li;
+    const int hx = hb * a.heads_per_block + x * 16 + li;
     if (hx >= a.H) return;
     const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
     uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
@@ -846,43 +927,46 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   };
   if (a.chunks == 1) {
+    if (!is_qk)
 #pragma unroll
-    for (int x = 0; x < kPair; ++x) store_out(x, O[x], l_run[x]);
+      for (int x = 0; x < kGroups; ++x) store_out(x, O[x], l_run[x]);
     return;
   }
   // Split chunks. Each workgroup counts itself in; the last one to arrive
-  // merges. The others publish their partials (each wave's accumulators as
-  // they sit in its registers, 1 KiB per store, then (reference, sum) of the
-  // block's heads), written through device-coherently, and count them
+  // merges. The others publish their partials (each PV wave's accumulators
+  // as they sit in its registers, 1 KiB per store, then (reference, sum) of
+  // the block's heads), written through device-coherently, and count them
   // published; the merger waits for that count. Only workgroups that have
   // already arrived are waited for, so the wait always ends; a bounded spin
   // turns a broken count into NaN output instead of a hang.
-  constexpr int kPartFloats = kPair * kCB * kWave * 4;  // per wave
+  constexpr int kPartFloats = kGroups * kCB * kWave * 4;  // per PV wave
   const size_t wg_slot = (size_t)(r * a.head_blocks + hb) * a.chunks;
   const int rh = r * a.head_blocks + hb;
   int32_t* arrived = a.ws_arrivals + rh;
   int32_t* published = a.ws_arrivals + (size_t)a.rows_hb + rh;
   auto part_o_of = [&](int cc) {
-    return a.part_o + ((wg_slot + cc) * kWaves + wave) * kPartFloats;
+    return a.part_o + ((wg_slot + cc) * kPVWaves + pw) * kPartFloats;
   };
   auto part_ml_of = [&](int cc, int x) {
-    return a.part_ml + ((wg_slot + cc) * a.heads_per_block + (pset * kPair + x) * 16 + li) * 2;
+    return a.part_ml + ((wg_slot + cc) * a.heads_per_block + x * 16 + li) * 2;
   };
   if (tid == 0) flag_sh = atomicAdd(arrived, 1) == a.chunks - 1 ? 2 : 0;
   __syncthreads();
   if (flag_sh != 2) {
-    float* po = part_o_of(c);
+    if (!is_qk) {
+      float* po = part_o_of(c);
 #pragma unroll
-    for (int x = 0; x < kPair; ++x)
+      for (int x = 0; x < kGroups; ++x)
 #pragma unroll
-      for (int j = 0; j < kCB; ++j) store_dev16(po + ((x * kCB + j) * kWave + lane) * 4, O[x][j]);
-    if (jbase == 0 && g == 0)
+        for (int j = 0; j < kCB; ++j) store_dev16(po + ((x * kCB + j) * kWave + lane) * 4, O[x][j]);
+      if (pw == 0 && g == 0)
 #pragma unroll
-      for (int x = 0; x < kPair; ++x) {
-        float* pml = part_ml_of(c, x);
-        store_dev(pml, m_run[x]);
-        store_dev(pml + 1, l_run[x]);
-      }
+        for (int x = 0; x < kGroups; ++x) {
+          float* pml = part_ml_of(c, x);
+          store_dev(pml, m_run[x]);
+          store_dev(pml + 1, l_run[x]);
+        }
+    }
     wait_vmcnt<0>();  // this wave's stores are complete before the barrier
     __syncthreads();
     if (tid == 0) {
@@ -908,25 +992,26 @@ void dsa_decode_kernel(DecodeArgs a) {
     __threadfence();
   }
   __syncthreads();
+  if (is_qk) return;
   const float poison = flag_sh == 2 ? 0.f : __builtin_nanf("");
   // Online log-sum-exp merge in fixed chunk order (deterministic whichever
   // chunk merges); each chunk's (reference, sum, partial) loads are issued
   // together.
-  float M[kPair], Ls[kPair];
-  f32x4 acc[kPair][kCB];
+  float M[kGroups], Ls[kGroups];
+  f32x4 acc[kGroups][kCB];
 #pragma unroll
-  for (int x = 0; x < kPair; ++x) {
+  for (int x = 0; x < kGroups; ++x) {
     M[x] = -INFINITY;
     Ls[x] = 0.f;
 #pragma unroll
     for (int j = 0; j < kCB; ++j) acc[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int cc = 0; cc < a.chunks; ++cc) {
-    float mc[kPair], lc[kPair];
-    f32x4 oc[kPair][kCB];
+    float mc[kGroups], lc[kGroups];
+    f32x4 oc[kGroups][kCB];
     if (cc == c) {
 #pragma unroll
-      for (int x = 0; x < kPair; ++x) {
+      for (int x = 0; x < kGroups; ++x) {
         mc[x] = m_run[x];
         lc[x] = l_run[x];
 #pragma unroll
@@ -935,7 +1020,7 @@ void dsa_decode_kernel(DecodeArgs a) {
     } else {
       const float* po = part_o_of(cc);
 #pragma unroll
-      for (int x = 0; x < kPair; ++x) {
+      for (int x = 0; x < kGroups; ++x) {
         const float* pml = part_ml_of(cc, x);
         mc[x] = pml[0];
         lc[x] = pml[1];
@@ -944,7 +1029,7 @@ void dsa_decode_kernel(DecodeArgs a) {
       }
     }
 #pragma unroll
-    for (int x = 0; x < kPair; ++x) {
+    for (int x = 0; x < kGroups; ++x) {
       if (mc[x] == -INFINITY) continue;  // empty chunk: its partial is zero
       const float mn = fmaxf(M[x], mc[x]);
       const float wold = M[x] == -INFINITY ? 0.f : fast_exp2(M[x] - mn);
@@ -956,7 +1041,7 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   }
 #pragma unroll
-  for (int x = 0; x < kPair; ++x) {
+  for (int x = 0; x < kGroups; ++x) {
 #pragma unroll
     for (int j = 0; j < kCB; ++j) acc[x][j] += poison;
     store_out(x, acc[x], Ls[x]);
@@ -975,7 +1060,7 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 
 template <int D, int kGroups>
 hipError_t launch_g(bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
-  const dim3 block(kParts * kGroups * kWave);
+  const dim3 block(4 * kGroups * kWave);
   if (split_v)
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
   else
@@ -988,6 +1073,7 @@ hipError_t launch_d(int groups, bool split_v, dim3 grid, hipStream_t st, const D
   return groups == 1 ? launch_g<D, 1>(split_v, grid, st, args)
                      : launch_g<D, 2>(split_v, grid, st, args);
 }
+
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
