@@ -275,11 +275,15 @@ void dsa_decode_kernel(DecodeArgs a) {
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
   constexpr int kCB = kDBlocks / kPVWaves;          // column blocks per PV wave (all groups)
   constexpr int kChunkMask = (kDBlocks < 16 ? kDBlocks : 16) - 1;
-  // Gather: a latent row is D/16 lanes of 16 bytes; the PV waves move the tiles.
+  // Gather: a latent row is D/16 lanes of 16 bytes. Every wave moves part of
+  // each tile (as many waves as there are DMA instructions per tile).
   constexpr int kLanesPerTok = D / 16;
   constexpr int kTokPerInstr = kWave / kLanesPerTok;
-  constexpr int kTPW = kTile / kPVWaves;            // tokens each PV wave DMAs per tile
-  constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per PV wave per tile
+  constexpr int kInstrPerTile = kTile / kTokPerInstr;
+  constexpr int kDmaWaves = kInstrPerTile < kWaves ? kInstrPerTile : kWaves;
+  constexpr int kTPW = kTile / kDmaWaves;           // tokens each DMA wave moves per tile
+  constexpr int kInstr = kTPW / kTokPerInstr;       // DMA instructions per DMA wave per tile
+  constexpr int kNd = kSplitV ? 2 * kInstr : kInstr;  // DMA instructions per wave per step
   // Selection: before the first tile the tile buffers hold the membership
   // bitmap of a window of positions (a quarter), each word's rank (a
   // quarter) and the row's block-table entries (the upper half).
@@ -333,8 +337,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   const int32_t* srow = a.sel + (size_t)r * a.width;
   // The length and up to 4 ids per thread are loaded first, from addresses
   // clamped into their buffers (no branches), then the row's block-table
-  // entries go straight into LDS; the query is loaded only once the ids are
-  // in, so that its traffic does not delay them.
+  // entries go straight into LDS, then this wave's share of the query.
   int L = a.seq_lens[r];
   int tpre[4];  // ids tid + u*kThreads (u < 4); the rest of a wider row is loaded per window
 #pragma unroll
@@ -362,8 +365,8 @@ void dsa_decode_kernel(DecodeArgs a) {
   static_assert(!kShareQ || kGroups * kKSteps * 4096 <= 2 * kTileBytes, "query exchange area");
   auto own_ks = [&](int i) { return kShareQ ? kQWaysPerGroup * i + qsub : i; };
   u32x4 qraw[kKOwn][4];
+  static_assert(kKOwn == 1, "one k-step of the query per wave (four 16-byte loads)");
   auto load_q = [&]() {
-    wait_vmcnt<0>();  // the block-table DMA (issued before) has landed
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (q_ok ? q_head : 0)) * D;
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
@@ -373,6 +376,10 @@ void dsa_decode_kernel(DecodeArgs a) {
       for (int v = 0; v < 4; ++v) qraw[i][v] = *(const u32x4*)(qrow + d0 + 8 * v);
     }
   };
+  load_q();
+  // the block-table DMA has landed once at most the four query loads issued
+  // after it are outstanding (the window loop's barriers then publish it)
+  wait_vmcnt<4 * kKOwn>();
 
   uint32_t* bitmap = (uint32_t*)smem;
   const DSA_LDS u32x4* bitmap4 = (const DSA_LDS u32x4*)smem;
@@ -381,7 +388,6 @@ void dsa_decode_kernel(DecodeArgs a) {
   const DSA_LDS uint32_t* wrank_l = (const DSA_LDS uint32_t*)(smem + kSmemBytes / 4);
   if (tid == 0) flag_sh = 0;
   int total = 0;
-  bool q_loaded = false;
   for (int base = 0; base < L; base += kWinWords * 32) {
     const int span = min(kWinWords * 32, L - base);
     const int nw4 = (((span + 31) >> 5) + 3) & ~3;                  // words in use
@@ -397,10 +403,6 @@ void dsa_decode_kernel(DecodeArgs a) {
       const int t = srow[j];
       if (t >= base && t - base < span)
         atomicOr(&bitmap[(t - base) >> 5], 1u << ((t - base) & 31));
-    }
-    if (!q_loaded) {
-      load_q();
-      q_loaded = true;
     }
     __syncthreads();
     // rank of each word: this thread's words are w0 .. w1 - 1; wave scan of
@@ -451,7 +453,6 @@ void dsa_decode_kernel(DecodeArgs a) {
     total += all;
     __syncthreads();  // the id table is complete; the bitmap is reused by the next window
   }
-  if (!q_loaded) load_q();
   const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
   const bool exporter = hb == 0;  // exports the ids and offsets of the row (after the loop)
@@ -476,13 +477,68 @@ void dsa_decode_kernel(DecodeArgs a) {
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * kThreads;
         if (i < n) {
-          rows_lds[i] = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
+          const uint32_t row = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
+          rows_lds[i] = row;
           if (exporter) ids_lds[i] = t[u];
+          // pad to whole tiles with the last real row (loaded, weighted by zero)
+          if (i == n - 1)
+            for (int p = n; p < ntiles * kTile; ++p) rows_lds[p] = row;
         }
       }
     }
   }
 
+  __syncthreads();  // the row table is complete (padded to whole tiles)
+
+  // -------------------------------------------------------------- 2. gather
+  // Wave w (< kDmaWaves) moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its
+  // instruction k writes kTokPerInstr consecutive LDS slots; DMA lane l
+  // carries chunk l % kLanesPerTok of token w*kTPW + (l / kLanesPerTok)*kInstr
+  // + k, so a lane's kInstr row indices are contiguous in the row table.
+  const DSA_LDS uint32_t* rows_l = (const DSA_LDS uint32_t*)rows_lds;
+  const bool dma_wave = wave < kDmaWaves;
+  const int pw_s = dma_wave ? wave : 0;
+  auto tile_rows = [&](int tile, uint32_t (&row)[kInstr]) {
+    const DSA_LDS uint32_t* rr =
+        rows_l + tile * kTile + pw_s * kTPW + (lane / kLanesPerTok) * kInstr;
+#pragma unroll
+    for (int k = 0; k < kInstr; ++k) row[k] = rr[k];
+  };
+  // Lane l carries chunk ci of token slot0 + j. slot0 is a multiple of
+  // kTokPerInstr (a power of two) and j < kTokPerInstr, so the token's
+  // swizzle is the uniform swizzle of slot0 XOR j: one per-lane constant.
+  const uint32_t dma_c0 =
+      (uint32_t)(((lane % kLanesPerTok) ^ ((lane / kLanesPerTok) & kChunkMask)) << 4);
+  auto dma_one = [&](int k, uint32_t row, int dst_off, const uint8_t* src,
+                     uint32_t c0) {
+    const int slot0 = pw_s * kTPW + k * kTokPerInstr;
+    const uint32_t chunk = c0 ^ ((uint32_t)tile_swizzle<D>(slot0) << 4);  // < D
+    const uint64_t off = (uint64_t)row * (uint64_t)D | (uint64_t)chunk;
+    dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
+  };
+  auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
+    uint32_t row[kInstr];
+    tile_rows(tile, row);
+#pragma unroll
+    for (int k = 0; k < kInstr; ++k) dma_one(k, row[k], dst_off, src, dma_c0);
+  };
+  // Token index (within the tile) held by LDS slot s.
+  auto token_of_slot = [&](int s) {
+    const int w = s / kTPW, sw = s % kTPW;
+    return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
+  };
+  // LDS byte offsets of the buffers holding tile i's K and V.
+  auto k_off = [&](int i) { return kSplitV ? (i & 1) * kTileBytes : (i & 3) * kTileBytes; };
+  auto v_off = [&](int i) { return kSplitV ? (2 + (i & 1)) * kTileBytes : (i & 3) * kTileBytes; };
+  // The first tiles (tile 0; with K and V the same bytes also tile 1) go out
+  // now; a separate V buffer is filled in the loop after every wave has read
+  // its query terms out of it.
+  auto issue_first = [&]() {
+    if (dma_wave) {
+      if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
+      if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
+    }
+  };
   // ---- the query as two FP8 terms under a per-head power-of-two scale that
   // puts the head's largest |q| in [128, 256)
   float amax = 0.f;
@@ -499,11 +555,12 @@ void dsa_decode_kernel(DecodeArgs a) {
         amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[i][v][e])), fabsf(bf16_hi(qraw[i][v][e]))));
   }
   amax = max_xor32(max_xor16(amax));
+  // The first tiles load while the query terms are prepared (issued after
+  // the query registers were first read, so that no wait for the query
+  // loads can also wait for these).
+  issue_first();
   if constexpr (kShareQ) xch_f[wave][lane] = amax;
-  __syncthreads();  // row table written (selection areas free); the groups' maxima visible
-  // pad to whole tiles with the last real row (loaded, weighted by zero)
-  if (n > 0)
-    for (int i = n + tid; i < ntiles * kTile; i += kThreads) rows_lds[i] = rows_lds[n - 1];
+  __syncthreads();  // the groups' maxima visible
   float score_scale;
   i32x8 qhi[kKSteps], qlo[kKSteps];
   {
@@ -547,56 +604,8 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
     score_scale = a.scale_log2 * pow2i(-sh);
   }
-  __syncthreads();  // row table padded; the groups' FP8 terms visible
+  __syncthreads();  // the groups' FP8 terms visible
 
-  // -------------------------------------------------------------- 2. gather
-  // PV wave p moves tokens [p*kTPW, (p+1)*kTPW) of a tile. Its instruction k
-  // writes kTokPerInstr consecutive LDS slots; DMA lane l carries chunk
-  // l % kLanesPerTok of token p*kTPW + (l / kLanesPerTok)*kInstr + k, so a
-  // lane's kInstr row indices are contiguous in the row table.
-  const DSA_LDS uint32_t* rows_l = (const DSA_LDS uint32_t*)rows_lds;
-  const int pw_s = wave % kPVWaves;
-  auto tile_rows = [&](int tile, uint32_t (&row)[kInstr]) {
-    const DSA_LDS uint32_t* rr =
-        rows_l + tile * kTile + pw_s * kTPW + (lane / kLanesPerTok) * kInstr;
-#pragma unroll
-    for (int k = 0; k < kInstr; ++k) row[k] = rr[k];
-  };
-  // Lane l carries chunk ci of token slot0 + j. slot0 is a multiple of
-  // kTokPerInstr (a power of two) and j < kTokPerInstr, so the token's
-  // swizzle is the uniform swizzle of slot0 XOR j: one per-lane constant.
-  const uint32_t dma_c0 =
-      (uint32_t)(((lane % kLanesPerTok) ^ ((lane / kLanesPerTok) & kChunkMask)) << 4);
-  auto dma_one = [&](int k, uint32_t row, int dst_off, const uint8_t* src,
-                     uint32_t c0) {
-    const int slot0 = pw_s * kTPW + k * kTokPerInstr;
-    const uint32_t chunk = c0 ^ ((uint32_t)tile_swizzle<D>(slot0) << 4);  // < D
-    const uint64_t off = (uint64_t)row * (uint64_t)D | (uint64_t)chunk;
-    dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
-  };
-  auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
-    uint32_t row[kInstr];
-    tile_rows(tile, row);
-#pragma unroll
-    for (int k = 0; k < kInstr; ++k) dma_one(k, row[k], dst_off, src, dma_c0);
-  };
-  // Token index (within the tile) held by LDS slot s.
-  auto token_of_slot = [&](int s) {
-    const int w = s / kTPW, sw = s % kTPW;
-    return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
-  };
-  // LDS byte offsets of the buffers holding tile i's K and V.
-  auto k_off = [&](int i) { return kSplitV ? (i & 1) * kTileBytes : (i & 3) * kTileBytes; };
-  auto v_off = [&](int i) { return kSplitV ? (2 + (i & 1)) * kTileBytes : (i & 3) * kTileBytes; };
-  // The first tiles (tile 0; with K and V the same bytes also tile 1) go out
-  // now; a separate V buffer is filled in the loop after every wave has read
-  // its query terms out of it.
-  auto issue_first = [&]() {
-    if (!is_qk) {
-      if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
-      if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
-    }
-  };
   if constexpr (kShareQ) {
     if (is_qk) {
       const u32x4* qx = (const u32x4*)(smem + kQxOff);
@@ -645,6 +654,35 @@ void dsa_decode_kernel(DecodeArgs a) {
     vswz[u] = tile_swizzle<D>(slot) << 4;
   }
 
+  // The gather of step it: tile it + 2 (or, with a separate V buffer, K of
+  // it + 1 and V of it), this wave's kNd instructions, spread by each role
+  // over its matrix steps so that the vector memory queue never stalls a
+  // wave for long. (The lane constant is laundered per step: the address
+  // arithmetic is then redone each time instead of being held in registers.)
+  auto dma_rows = [&](int it, uint32_t (&drow)[kNd]) {
+    if (kSplitV ? it + 1 < ntiles : it + 2 < ntiles) {
+      uint32_t rk[kInstr];
+      tile_rows(kSplitV ? it + 1 : it + 2, rk);
+#pragma unroll
+      for (int k = 0; k < kInstr; ++k) drow[k] = rk[k];
+    }
+    if (kSplitV && it < ntiles) {
+      uint32_t rv[kInstr];
+      tile_rows(it, rv);
+#pragma unroll
+      for (int k = 0; k < kInstr; ++k) drow[kNd - kInstr + k] = rv[k];
+    }
+  };
+  auto dma_step = [&](int it, int d, const uint32_t (&drow)[kNd], uint32_t c0) {
+    if (!dma_wave) return;
+    if (d < kInstr) {
+      if (kSplitV ? it + 1 < ntiles : it + 2 < ntiles)
+        dma_one(d, drow[d], k_off(kSplitV ? it + 1 : it + 2), a.k_cache, c0);
+    } else {
+      if (kSplitV && it < ntiles) dma_one(d - kInstr, drow[d], v_off(it), a.v_cache, c0);
+    }
+  };
+
   // -------------------------------------------------------------- 3. attend
   // Step i scores tile i (scoring waves) and accumulates tile i - 1 (PV
   // waves), between one barrier and the next. The accumulators are touched
@@ -685,10 +723,19 @@ void dsa_decode_kernel(DecodeArgs a) {
     for (int pass = 0; pass < 2; ++pass) {
       l_part = 0.f;
       bool overflow = false;
+      if (pass == 1) issue_first();
         for (int it = 0; it <= ntiles; ++it) {
-          // tile it's K in LDS; every read of the weights of it - 2 done
+          // this wave's share of tile it has landed (the next tile's may
+          // still be in flight); after the barrier tile it's K is in LDS and
+          // every read of the weights of it - 2 is done
+          if (!kSplitV && it + 1 < ntiles) wait_vmcnt<kInstr>();
+          else wait_vmcnt<0>();
           barrier_lds();
           const bool score = it < ntiles;
+          uint32_t drow[kNd];
+          uint32_t c0 = dma_c0;
+          asm volatile("" : "+v"(c0));
+          if (dma_wave) dma_rows(it, drow);
 
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
@@ -721,6 +768,8 @@ void dsa_decode_kernel(DecodeArgs a) {
             for (int s = 0; s < kSteps; ++s) {
               const int k = s / kKSteps, ks = s % kKSteps;
               if (s + kKPre < kSteps) kbuf[(s + kKPre) % (kKPre + 1)] = load_k(s + kKPre);
+#pragma unroll
+              for (int d = s * kNd / kSteps; d < (s + 1) * kNd / kSteps; ++d) dma_step(it, d, drow, c0);
               __builtin_amdgcn_sched_barrier(0);
               if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
               S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qhi[ks], S[k]);
@@ -793,7 +842,7 @@ void dsa_decode_kernel(DecodeArgs a) {
       for (int x = 0; x < kGroups; ++x)
 #pragma unroll
         for (int j = 0; j < kCB; ++j) O[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      issue_first();
+      if (pass == 1) issue_first();
         for (int it = 0; it <= ntiles; ++it) {
           // Tile it has landed: wait for every DMA of this wave but the next
           // tile's, then the barrier (tile it - 1's V and weights visible,
@@ -803,39 +852,13 @@ void dsa_decode_kernel(DecodeArgs a) {
           barrier_lds();
           if (pass == 0 && it == 0) barrier_lds();  // the scoring waves' reference exchange
 
-          // ---- gather: tile it + 2 (or, with a separate V buffer, K of it +
-          // 1 and V of it), its instructions spread over the PV steps below
-          // so that the vector memory queue never stalls this wave for long.
-          // (The lane constant is laundered per step: address arithmetic is
-          // then redone each time instead of being held in registers.)
+          uint32_t drow[kNd];
           uint32_t c0 = dma_c0;
           asm volatile("" : "+v"(c0));
-          constexpr int kNd = kSplitV ? 2 * kInstr : kInstr;
-          const bool dk = kSplitV ? it + 1 < ntiles : it + 2 < ntiles;
-          const bool dv = kSplitV && it < ntiles;
-          uint32_t drow[kNd];
-          if (dk) {
-            uint32_t rk[kInstr];
-            tile_rows(kSplitV ? it + 1 : it + 2, rk);
-#pragma unroll
-            for (int k = 0; k < kInstr; ++k) drow[k] = rk[k];
-          }
-          if (dv) {
-            uint32_t rv[kInstr];
-            tile_rows(it, rv);
-#pragma unroll
-            for (int k = 0; k < kInstr; ++k) drow[kNd - kInstr + k] = rv[k];
-          }
-          auto dma_step = [&](int d) {
-            if (d < kInstr) {
-              if (dk) dma_one(d, drow[d], k_off(kSplitV ? it + 1 : it + 2), a.k_cache, c0);
-            } else {
-              if (dv) dma_one(d - kInstr, drow[d], v_off(it), a.v_cache, c0);
-            }
-          };
+          if (dma_wave) dma_rows(it, drow);
           if (it == 0) {
 #pragma unroll
-            for (int d = 0; d < kNd; ++d) dma_step(d);
+            for (int d = 0; d < kNd; ++d) dma_step(it, d, drow, c0);
             continue;
           }
           // ---- O^T += V^T P^T for tile it - 1 over this wave's column
@@ -872,7 +895,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           for (int j0 = 0; j0 < kCB; ++j0) {
             if (j0 + kVPre < kCB) vbuf[(j0 + kVPre) % (kVPre + 1)] = load_v(j0 + kVPre);
 #pragma unroll
-            for (int d = j0 * kNd / kCB; d < (j0 + 1) * kNd / kCB; ++d) dma_step(d);
+            for (int d = j0 * kNd / kCB; d < (j0 + 1) * kNd / kCB; ++d) dma_step(it, d, drow, c0);
             __builtin_amdgcn_sched_barrier(0);
             const i32x8& vop = vbuf[j0 % (kVPre + 1)];
 #pragma unroll
