@@ -6,8 +6,9 @@
 //   [build]    "spark_model/layers/glm5next_dsa/build.rs"
 // How it is computed is this library's own design for CDNA4 (wave64, FP8
 // matrix cores, 160 KiB LDS, LDS DMA, transposing LDS reads). One kernel does
-// the whole decode. A workgroup owns one (row, block of up to 64 heads, chunk
-// of the row's selected set) and runs two waves per 16-head group:
+// the whole decode. A workgroup owns one (row, block of up to 32 heads, chunk
+// of the row's selected set) and runs eight waves: per 16-head group two
+// scoring waves, and four PV waves shared by the groups.
 //
 //   1. selection   the row's ids become a set through an LDS bitmap over
 //                  [0, seq_len): holes, repeats and out-of-range ids vanish
@@ -16,23 +17,25 @@
 //                  its chunk and translates each through the block table to
 //                  the index of its FP8 latent row ([decode_k], slot of a
 //                  position).
-//   2. gather      128-token tiles of latent rows are DMA'd straight from HBM
-//                  into LDS; the next tile is in flight while one is consumed.
+//   2. gather      64-token tiles of latent rows are DMA'd straight from HBM
+//                  into LDS (four buffers: one tile scored, one accumulated,
+//                  two in flight).
 //   3. attend      both contractions run on the FP8 matrix cores (16x16x128,
 //                  fp32 accumulation) over the cached bytes as they are:
-//                    S^T = K Q^T   the two waves of a head group each score
-//                                  half of the tile's tokens. Q (bf16) enters
-//                                  as an exact sum of two FP8 terms under a
-//                                  per-head power-of-two scale;
-//                    O^T = V^T P^T each wave then accumulates half of the
-//                                  latent columns over all of the tile's
-//                                  tokens. The softmax weights enter as two
-//                                  FP8 terms (relative error <= 2^-9, below
-//                                  bf16's 2^-8) under per-block E8M0
-//                                  exponents, exchanged between the two waves
-//                                  through LDS; V comes from ds_read_b64_tr_b8,
-//                                  which hands each lane 8 tokens of one
-//                                  latent column.
+//                    S^T = K Q^T   the two scoring waves of a head group each
+//                                  score half of the tile's tokens. Q (bf16)
+//                                  enters as an exact sum of two FP8 terms
+//                                  under a per-head power-of-two scale;
+//                    O^T = V^T P^T each PV wave accumulates a quarter of the
+//                                  latent columns, for every head group, over
+//                                  all of the tile's tokens, one tile behind
+//                                  the scoring. The softmax weights enter as
+//                                  two FP8 terms (relative error <= 2^-9,
+//                                  below bf16's 2^-8) under an E8M0 exponent
+//                                  per 16-token block and head, exchanged
+//                                  through LDS; V comes from
+//                                  ds_read_b64_tr_b8, which hands each lane 8
+//                                  tokens of one latent column.
 //                  Weights are taken against a fixed per-head reference (the
 //                  first tile's max); the block exponents absorb later
 //                  growth, so the accumulators are never rescaled.
@@ -164,17 +167,30 @@ __device__ __forceinline__ void store_dev16(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
+// Maximum of two values that are never NaN, as one median-of-three against
+// +inf: the compiler's maximum first quiets each operand (one more
+// instruction apiece). The +inf is passed in a register the compiler cannot
+// see through, so that the median is not turned back into that maximum.
+__device__ __forceinline__ float opaque_inf() {
+  float x = INFINITY;
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ float max2(float a, float b, float pinf) {
+  return __builtin_amdgcn_fmed3f(a, b, pinf);
+}
+
 // Max / sum over lane pairs 16 (resp. 32) apart through the cross-row lane
 // swaps (no LDS traffic).
-__device__ __forceinline__ float max_xor16(float x) {
+__device__ __forceinline__ float max_xor16(float x, float pinf = INFINITY) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]), pinf);
 }
-__device__ __forceinline__ float max_xor32(float x) {
+__device__ __forceinline__ float max_xor32(float x, float pinf = INFINITY) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]), pinf);
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
@@ -298,9 +314,9 @@ void dsa_decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
   __shared__ __attribute__((aligned(16))) int32_t ids_lds[kMaxChunkTokens];
-  // softmax weights of a tile as PV B operands: [tile parity][group][hi|lo][lane] x 16 bytes
+  // softmax weights of a tile as PV B operands: [tile parity][group][operand half][lane] x 16 bytes
   __shared__ __attribute__((aligned(16))) i32x4 xch_p[2][kGroups][2][kWave];
-  __shared__ int xch_e[2][kGroups][kParts][16];  // their E8M0 exponent bytes, per head
+  __shared__ int xch_e[2][kGroups][4][16];  // their E8M0 exponent bytes, per 16-token block and head
   __shared__ float xch_f[kWaves][kWave];         // per-head scalars between waves
   __shared__ float xch_m[kGroups][kWave];        // per-head reference, for the PV waves
   __shared__ int scan_sh[kWaves];
@@ -633,25 +649,25 @@ void dsa_decode_kernel(DecodeArgs a) {
     for (int h = 0; h < 2; ++h)
       kofs[p][h] = 32 * D * part + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
 
-  // PV operands. B (the weights, per head): lane group g holds the 16
-  // tokens T_g of tile half g >> 1 that scoring lane groups (g & 1) and
-  // (g & 1) + 2 of that half score, as bytes 0-15 (hi terms) and 16-31 (lo
-  // terms). The operand's four exponent blocks are then {hi, lo} x {half 0,
-  // half 1}: each the weights of one scoring wave for the head. A (V): lane
-  // group g needs the same 16 tokens' latent column in bytes 0-15 and again
-  // in 16-31. Byte i of the 8 supplied by scoring lane group g' of half P is
-  // slot 32*P + 16*(i >> 2) + 4*g' + (i & 3). A transposing read hands lane
-  // li the 8 bytes of its column from 8 rows; lanes 2k and 2k+1 of the
-  // 16-lane group supply row k (column halves 0 and 1). (Lane groups 0 and
-  // 1, read together, cover distinct swizzled chunk positions, as do 2 and
-  // 3.)
+  // PV operands. The matrix core scales B (the weights) in four blocks of
+  // 32 k-positions: bytes 0-15 (then 16-31) of lane groups {0, 1} (then
+  // {2, 3}); lane group G supplies block G's exponent. Each block carries
+  // one 16-token block of the tile, its hi terms and its lo terms, so the 16
+  // tokens of a head share one exponent. In lane group G, bytes 16*h ..
+  // 16*h + 7 hold the hi terms of slots 32*h + 8*G .. +7 and bytes 16*h + 8
+  // .. +15 their lo terms: slots 32*h + 8*G + 4*(g & 1) + i come from
+  // scoring lane group g of block 2*h + (G >> 1), byte 4*(g & 1) + i. A (V):
+  // lane group G needs the latent column of those 8 slots twice per half. A
+  // transposing read hands lane li the 8 bytes of its column from 8 rows;
+  // lanes 2k and 2k+1 of the 16-lane group supply row k (column halves 0 and
+  // 1). (Lane groups 0 and 1, read together, cover 16 consecutive slots and
+  // so distinct swizzled chunk positions, as do 2 and 3.)
   int vrow[2], vswz[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int P = g >> 1, gp = (g & 1) + 2 * u, rr = li >> 1;
-    const int slot = 32 * P + 16 * (rr >> 2) + 4 * gp + (rr & 3);
-    vrow[u] = slot * D + 8 * (li & 1);
-    vswz[u] = tile_swizzle<D>(slot) << 4;
+  for (int h = 0; h < 2; ++h) {
+    const int slot = 32 * h + 8 * g + (li >> 1);
+    vrow[h] = slot * D + 8 * (li & 1);
+    vswz[h] = tile_swizzle<D>(slot) << 4;
   }
 
   // The gather of step it: tile it + 2 (or, with a separate V buffer, K of
@@ -696,6 +712,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   f32x4 O[kGroups][kCB];
   float l_part = 0.f;        // this scoring wave's share of sum_t 2^(s_t - m_ref), per head
   float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
+  float mb7 = -7.f;          // (m_ref, or 0 while it is -inf) - 7
   float m_seen = -INFINITY;  // exact max of this wave's scores so far
   // After the first pass: recompute the chunk only if some scoring wave saw
   // a score beyond the slack (every wave takes part; two barriers).
@@ -709,6 +726,7 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
       m_ref = m;
+      mb7 = (m_ref == -INFINITY ? 0.f : m_ref) - 7.f;
     }
     __syncthreads();
     return redo;
@@ -720,6 +738,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // i - 1. Each role keeps its own registers (the query terms, the
   // accumulators) inside its own branch.
   if (is_qk) {
+    const float pinf = opaque_inf();
     for (int pass = 0; pass < 2; ++pass) {
       l_part = 0.f;
       bool overflow = false;
@@ -740,7 +759,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
           f32x4 S[2];
-          float mh = -INFINITY;
+          float mh[2] = {-INFINITY, -INFINITY};  // per 16-token block
           if (score) {
             const DSA_LDS uint8_t* kt = lds + k_off(it);
             constexpr int kSteps = 2 * kKSteps;
@@ -787,51 +806,48 @@ void dsa_decode_kernel(DecodeArgs a) {
                   if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
             }
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-              mh = fmaxf(mh, fmaxf(fmaxf(S[k][0], S[k][1]), fmaxf(S[k][2], S[k][3])));
-            mh = max_xor32(max_xor16(mh)) * score_scale;  // score_scale > 0
-            m_seen = fmaxf(m_seen, mh);
+            for (int k = 0; k < 2; ++k) {
+              const float m4 = max2(max2(S[k][0], S[k][1], pinf), max2(S[k][2], S[k][3], pinf), pinf);
+              mh[k] = max_xor32(max_xor16(m4, pinf), pinf) * score_scale;  // score_scale > 0
+              m_seen = max2(m_seen, mh[k], pinf);
+            }
           }
           if (pass == 0 && it == 0) {
             // first tile: the reference is the tile's max over the group's
             // scoring waves
-            if (score) xch_f[wave][lane] = mh;
+            if (score) xch_f[wave][lane] = fmaxf(mh[0], mh[1]);
             barrier_lds();
             if (ntiles > 0) {
               float m = -INFINITY;
 #pragma unroll
               for (int p = 0; p < kParts; ++p) m = fmaxf(m, xch_f[hg + kGroups * p][lane]);
               m_ref = m;
+              mb7 = (m_ref == -INFINITY ? 0.f : m_ref) - 7.f;
             }
           }
           if (score) {
-            // ---- weights: the wave's largest weight of the head maps to [128, 256)
-            overflow |= mh > m_ref + kSlack;
-            const float mbase = m_ref == -INFINITY ? 0.f : m_ref;
-            int e = mh == -INFINITY ? 0 : (int)floorf(mh - mbase);
-            e = e < -100 ? -100 : (e > 100 ? 100 : e);
-            const float bsub = mbase + (float)(e - 7);
-            i32x2 phi, plo;
-            float lsum = 0.f;
+            // ---- weights, per 16-token block: the block's largest weight of
+            // the head maps to [128, 256) (a block with no valid token:
+            // exponent -100, weights 0)
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
+              const float ef = floorf(__builtin_amdgcn_fmed3f(mh[k] - (mb7 + 7.f), -100.f, 100.f));
+              overflow |= ef >= kSlack;
+              const float bsub = mb7 + ef;
+              const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
               float p[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
-              lsum += (p[0] + p[1]) + (p[2] + p[3]);
-              int hi, lo;
-              split_fp8x4(p[0], p[1], p[2], p[3], hi, lo);
-              phi[k] = hi;
-              plo[k] = lo;
+              l_part += ((p[0] + p[1]) + (p[2] + p[3])) * __uint_as_float((uint32_t)eb << 23);
+              int phi, plo;
+              split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
+              // block b = 2*part + k: word (g & 1) (hi) and 2 + (g & 1) (lo)
+              // of PV lane group 2*k + (g >> 1), operand half part, head li
+              int* dst = (int*)&xch_p[it & 1][hg][part][(2 * k + (g >> 1)) * 16 + li];
+              dst[g & 1] = phi;
+              dst[2 + (g & 1)] = plo;
+              if (g == 0) xch_e[it & 1][hg][2 * part + k][li] = eb;
             }
-            l_part += lsum * pow2i(e - 7);
-            // this lane's 8 bytes are bytes 8*(g >> 1) .. +7 (hi terms) and
-            // 16 + 8*(g >> 1) .. (lo terms) of PV lane group 2*part + (g & 1),
-            // head li
-            const int pl = (2 * part + (g & 1)) * 16 + li;
-            ((i32x2*)&xch_p[it & 1][hg][0][pl])[g >> 1] = phi;
-            ((i32x2*)&xch_p[it & 1][hg][1][pl])[g >> 1] = plo;
-            if (g == 0) xch_e[it & 1][hg][part][li] = e + 120;
           }
         }
       if (pass == 0 && !redo_needed(overflow)) break;
@@ -869,9 +885,9 @@ void dsa_decode_kernel(DecodeArgs a) {
           int psc[kGroups];
 #pragma unroll
           for (int x = 0; x < kGroups; ++x) {
-            const i32x4 h = xch_p[pt & 1][x][0][lane], l = xch_p[pt & 1][x][1][lane];
-            pB[x] = i32x8{h.x, h.y, h.z, h.w, l.x, l.y, l.z, l.w};
-            psc[x] = xch_e[pt & 1][x][g & 1][li];
+            const i32x4 h0 = xch_p[pt & 1][x][0][lane], h1 = xch_p[pt & 1][x][1][lane];
+            pB[x] = i32x8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+            psc[x] = xch_e[pt & 1][x][g][li];
           }
           const DSA_LDS uint8_t* vt = lds + v_off(pt);
           auto load_v = [&](int j0) -> i32x8 {
@@ -880,10 +896,10 @@ void dsa_decode_kernel(DecodeArgs a) {
             for (int u = 0; u < 2; ++u) {
               const int addr = (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
               const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
-              vop[2 * u] = v2.x;
-              vop[2 * u + 1] = v2.y;
-              vop[4 + 2 * u] = v2.x;
-              vop[4 + 2 * u + 1] = v2.y;
+              vop[4 * u] = v2.x;      // against the hi terms
+              vop[4 * u + 1] = v2.y;
+              vop[4 * u + 2] = v2.x;  // against the lo terms
+              vop[4 * u + 3] = v2.y;
             }
             return vop;
           };
