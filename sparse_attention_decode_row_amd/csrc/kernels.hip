@@ -254,6 +254,7 @@ struct DecodeArgs {
   int bt_stride;
   int bt_entries;    // block-table entries a row needs: ceil(max_seq_len / block_size)
   int block_size;
+  int bs_shift;      // log2(block_size) when it is a power of two, else -1
   int chunks;
   int chunk_tokens;
   int chunk_lead;    // extra tokens of chunk 0 (ranks shift by this for c > 0)
@@ -393,6 +394,7 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   };
   load_q();
+
   // the block-table DMA has landed once at most the four query loads issued
   // after it are outstanding (the window loop's barriers then publish it)
   wait_vmcnt<4 * kKOwn>();
@@ -403,6 +405,8 @@ void dsa_decode_kernel(DecodeArgs a) {
   u32x4* wrank4 = (u32x4*)(smem + kSmemBytes / 4);
   const DSA_LDS uint32_t* wrank_l = (const DSA_LDS uint32_t*)(smem + kSmemBytes / 4);
   if (tid == 0) flag_sh = 0;
+  const bool exporter = hb == 0;  // exports the ids and offsets of the row (after the loop)
+  const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
   int total = 0;
   for (int base = 0; base < L; base += kWinWords * 32) {
     const int span = min(kWinWords * 32, L - base);
@@ -455,12 +459,21 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
     // Each id finds its own rank: its word's rank plus the set bits below it
-    // in the word. Repeats of an id write the same entry with the same value.
+    // in the word, and goes straight through the block table (the entries
+    // in LDS; global memory for a page beyond them) to the index of its
+    // latent row (page * rows per page + slot in page). Repeats of an id
+    // write the same entries with the same values.
     auto place = [&](int t) {
       if (t >= base && t - base < span) {
         const int o = t - base, w = o >> 5;
         const int rank = total + (int)wrank_l[w] + __popc(bitmap_l[w] & ((1u << (o & 31)) - 1u));
-        if (rank >= cstart && rank < cend) rows_lds[rank - cstart] = (uint32_t)t;
+        if (rank >= cstart && rank < cend) {
+          const int pi = a.bs_shift >= 0 ? t >> a.bs_shift : t / a.block_size;
+          const int slot = t - pi * a.block_size;
+          const uint32_t page = (uint32_t)(pi < nbt ? btl[pi] : bt[pi]);
+          rows_lds[rank - cstart] = page * a.stride_rows + (uint32_t)slot;
+          if (exporter) ids_lds[rank - cstart] = t;
+        }
       }
     };
 #pragma unroll
@@ -471,38 +484,11 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
   const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
-  const bool exporter = hb == 0;  // exports the ids and offsets of the row (after the loop)
 
-  // ids -> latent row indices (page * rows per page + slot in page) through
-  // the block-table entries in LDS (global memory for a page beyond them).
-  {
-    const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
-    for (int i0 = tid; i0 < n; i0 += 4 * kThreads) {
-      int t[4];
-      uint32_t page[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        t[u] = i0 + u * kThreads < n ? (int)rows_lds[i0 + u * kThreads] : 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        t[u] = min(max(t[u], 0), L - 1);  // a no-op for every id the bitmap produced
-        const int pi = t[u] / a.block_size;
-        page[u] = i0 + u * kThreads < n ? (uint32_t)(pi < nbt ? btl[pi] : bt[pi]) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kThreads;
-        if (i < n) {
-          const uint32_t row = page[u] * a.stride_rows + (uint32_t)(t[u] % a.block_size);
-          rows_lds[i] = row;
-          if (exporter) ids_lds[i] = t[u];
-          // pad to whole tiles with the last real row (loaded, weighted by zero)
-          if (i == n - 1)
-            for (int p = n; p < ntiles * kTile; ++p) rows_lds[p] = row;
-        }
-      }
-    }
-  }
+  // pad the row table to whole tiles with the last real row (loaded,
+  // weighted by zero)
+  if (n > 0)
+    for (int p = n + tid; p < ntiles * kTile; p += kThreads) rows_lds[p] = rows_lds[n - 1];
 
   __syncthreads();  // the row table is complete (padded to whole tiles)
 
@@ -1227,6 +1213,7 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.bt_stride = p.block_table_stride;
   da.bt_entries = (int)(((int64_t)p.max_seq_len + p.block_size - 1) / p.block_size);
   da.block_size = p.block_size;
+  da.bs_shift = (p.block_size & (p.block_size - 1)) == 0 ? __builtin_ctz((unsigned)p.block_size) : -1;
   da.chunks = plan->chunks;
   da.chunk_tokens = plan->chunk_tokens;
   da.chunk_lead = plan->chunk_lead;
