@@ -56,6 +56,13 @@ def lib() -> ctypes.CDLL:
             [ctypes.c_double] * 3 + [ctypes.c_void_p] * 7 + [ctypes.c_int32])
         L.dsa_oracle_max_threads.restype = ctypes.c_int32
         L.dsa_oracle_max_threads.argtypes = []
+        L.dsa_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
+        L.dsa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_double]
+        L.dsa_oracle_latent_write.restype = ctypes.c_int
+        L.dsa_oracle_latent_write.argtypes = (
+            [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+             ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_double,
+             ctypes.c_double, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p])
         _lib = L
     return _lib
 
@@ -95,6 +102,36 @@ def token_offset(bt_row, t: int, block_size: int, cache_stride_bytes: int,
                                              int(block_size),
                                              int(cache_stride_bytes),
                                              int(kv_lora_rank)))
+
+
+def fp8_e4m3fn_encode(values) -> np.ndarray:
+    """Nearest FP8 E4M3FN codes (ties to even, saturating at +-448), one call
+    per value."""
+    L = lib()
+    flat = np.asarray(values, dtype=np.float64).ravel()
+    out = np.array([L.dsa_oracle_fp8_e4m3fn_encode(float(v)) for v in flat], dtype=np.uint8)
+    return out.reshape(np.shape(values))
+
+
+def latent_write(kv_a_bits, weight_bits, slots, pool, *, block_size: int,
+                 cache_stride_bytes: int, eps: float, inv_kv_scale: float):
+    """The cache writer: writes the FP8 rows into `pool` (uint8, modified in
+    place) and returns the pre-quantisation values [rows, D] (float64)."""
+    kv_a_bits = _c(kv_a_bits, np.uint16)
+    R, D = kv_a_bits.shape
+    w = _c(weight_bits, np.uint16).ravel()
+    sl = _c(slots, np.int64).ravel()
+    assert w.size == D and sl.size == R
+    assert pool.dtype == np.uint8 and pool.flags["C_CONTIGUOUS"]
+    values = np.zeros((R, D), dtype=np.float64)
+    rc = lib().dsa_oracle_latent_write(R, D, kv_a_bits.ctypes.data, w.ctypes.data,
+                                       sl.ctypes.data, int(block_size),
+                                       int(cache_stride_bytes), float(eps),
+                                       float(inv_kv_scale), pool.ctypes.data,
+                                       pool.size, values.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle latent_write rejected its arguments (rc={rc})")
+    return values
 
 
 def max_threads() -> int:

@@ -184,3 +184,64 @@ int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
   free(ids); free(offs); free(count);
   return fail ? -1 : 0;
 }
+
+/* Nearest finite E4M3FN code by exhaustive search over the 127 non-negative
+ * finite codes (their values increase with the code), ties to the even
+ * mantissa field; beyond 448, 448 (saturating). */
+uint8_t dsa_oracle_fp8_e4m3fn_encode(double x) {
+  const int neg = signbit(x) ? 1 : 0;
+  const double a = fabs(x);
+  int best = 0;
+  double best_err = INFINITY;
+  if (a >= 448.0) {
+    best = 0x7E;
+  } else {
+    for (int c = 0; c <= 0x7E; ++c) {
+      const double err = fabs(dsa_oracle_fp8_e4m3fn((uint8_t)c) - a);
+      if (err < best_err || (err == best_err && (c & 1) == 0)) {
+        best_err = err;
+        best = c;
+      }
+    }
+  }
+  return (uint8_t)(best | (neg << 7));
+}
+
+/* [decode_k] latent_write: RMSNorm of the kv_a row times the layernorm
+ * weight, scaled by 1/kv_scale, quantised to FP8 into the token's slot of the
+ * paged pool. Plain double arithmetic in index order. */
+int dsa_oracle_latent_write(int32_t rows, int32_t kv_lora_rank,
+                            const uint16_t* kv_a, const uint16_t* weight,
+                            const int64_t* slots, int32_t block_size,
+                            uint64_t cache_stride_bytes, double eps,
+                            double inv_kv_scale, uint8_t* pool,
+                            uint64_t pool_bytes, double* values) {
+  const int32_t D = kv_lora_rank;
+  if (rows < 0 || D <= 0 || block_size <= 0 || !(eps >= 0.0)) return -1;
+  if (rows > 0 && (!kv_a || !weight || !slots || !pool)) return -1;
+  if (cache_stride_bytes == 0) cache_stride_bytes = (uint64_t)block_size * (uint64_t)D;
+  for (int32_t i = 0; i < rows; ++i) {
+    const uint16_t* x = kv_a + (size_t)i * D;
+    double* yv = values ? values + (size_t)i * D : NULL;
+    const int64_t slot = slots[i];
+    if (slot < 0) {
+      if (yv) for (int32_t d = 0; d < D; ++d) yv[d] = 0.0;
+      continue;
+    }
+    const uint64_t off = (uint64_t)(slot / block_size) * cache_stride_bytes +
+                         (uint64_t)(slot % block_size) * (uint64_t)D;
+    if (off + (uint64_t)D > pool_bytes) return -1;
+    double ss = 0.0;
+    for (int32_t d = 0; d < D; ++d) {
+      const double v = dsa_oracle_bf16(x[d]);
+      ss += v * v;
+    }
+    const double inv_rms = 1.0 / sqrt(ss / (double)D + eps);
+    for (int32_t d = 0; d < D; ++d) {
+      const double y = dsa_oracle_bf16(x[d]) * inv_rms * dsa_oracle_bf16(weight[d]) * inv_kv_scale;
+      if (yv) yv[d] = y;
+      pool[off + (uint64_t)d] = dsa_oracle_fp8_e4m3fn_encode(y);
+    }
+  }
+  return 0;
+}

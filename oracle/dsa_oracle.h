@@ -15,9 +15,10 @@
  *   [build]    page "spark_model/layers/glm5next_dsa/build.rs"
  *
  * Parity status: every function here is pinned by CPU tests against
- * something other than itself (torch's float8 cast, Python set semantics,
- * a dense masked-attention brute force over a logically contiguous cache,
- * closed forms). None is "parity unpinned".
+ * something other than itself (torch's float8 casts in both directions,
+ * Python set semantics, a dense masked-attention brute force over a logically
+ * contiguous cache, closed forms of the RMS normalisation, hand-placed
+ * slots). None is "parity unpinned".
  */
 #ifndef DSA_ORACLE_H
 #define DSA_ORACLE_H
@@ -79,6 +80,30 @@ int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
 
 /* Number of threads an OpenMP parallel region of the decode would use. */
 int32_t dsa_oracle_max_threads(void);
+
+/* FP8 E4M3FN code of x, rounded to the nearest finite code (ties to the code
+ * with an even mantissa field) and saturated to +-448 beyond the largest
+ * finite value (never NaN). The sign of a zero result is the sign of x. This
+ * is how latent rows are quantised into the cache (value / kv_scale, stored
+ * as FP8; [decode_k] latent_write launch). x must not be NaN. */
+uint8_t dsa_oracle_fp8_e4m3fn_encode(double x);
+
+/* The cache writer ([decode_k] latent_write launch: one kv_a row, the
+ * kv_a_layernorm weight, the pool, the token's slot, rms_eps, 1/kv_scale).
+ * For each row i with slots[i] >= 0 (a negative slot writes nothing):
+ *   y_d = x_d / sqrt(mean_d(x_d^2) + eps) * w_d * inv_kv_scale
+ * with x = kv_a[i] and w both bf16 bits, computed in double; the FP8 codes
+ * of y (dsa_oracle_fp8_e4m3fn_encode) go to the pool bytes
+ *   (slot / block_size) * cache_stride_bytes + (slot mod block_size) * D
+ * (the decode's addressing of a token row). values, if not NULL, receives y
+ * as [rows, D] doubles (rows with a negative slot: 0). Returns 0, or -1 on a
+ * bad argument or a row that would fall outside pool_bytes. */
+int dsa_oracle_latent_write(int32_t rows, int32_t kv_lora_rank,
+                            const uint16_t* kv_a, const uint16_t* weight,
+                            const int64_t* slots, int32_t block_size,
+                            uint64_t cache_stride_bytes, double eps,
+                            double inv_kv_scale, uint8_t* pool,
+                            uint64_t pool_bytes, double* values);
 
 #ifdef __cplusplus
 }
