@@ -213,13 +213,39 @@ int dsa_decode_timing_begin(dsa_decode_plan_t plan, int32_t max_launches);
 int dsa_decode_timing_end(dsa_decode_plan_t plan, float* kernel_ms,
                           int32_t* launches);
 
+/* The cache writer ([decode_k] latent_write launch, which passes one kv_a
+ * row, the kv_a_layernorm weight, the pool, the token's slot, rms_eps and
+ * 1/kv_scale). For each row i < num_rows with slots[i] >= 0:
+ *   y_d = x_d / sqrt(mean_d(x_d^2) + rms_eps) * w_d * inv_kv_scale
+ * computed in fp32, rounded to FP8 E4M3FN (nearest, ties to even, saturating
+ * at +-448, never NaN) and stored at byte
+ *   (slot / block_size) * cache_stride_bytes + (slot mod block_size) * D
+ * of k_pool (the decode's addressing of a token row; the slot of a position
+ * is physical page * block_size + position mod block_size). A negative slot
+ * writes nothing. Device pointers, caller-owned:
+ *   kv_a     bf16  [num_rows, kv_lora_rank], 16-byte aligned
+ *   weight   bf16  [kv_lora_rank], 16-byte aligned
+ *   slots    int64 [num_rows]
+ *   k_pool   FP8 E4M3FN pool, 16-byte aligned
+ * cache_stride_bytes 0 means block_size * kv_lora_rank; otherwise at least
+ * that and a multiple of 16. rms_eps >= 0 and inv_kv_scale > 0, finite.
+ * Enqueued on `stream` (NULL = default); nothing is allocated or retained.
+ * num_rows == 0 is a no-op. Device-side precondition (not checked): every
+ * slot's row lies inside the pool. Errors: DSA_DECODE_ERR_INVALID,
+ * DSA_DECODE_ERR_UNSUPPORTED (kv_lora_rank), DSA_DECODE_ERR_LAUNCH. */
+int dsa_decode_latent_write(const void* kv_a, const void* weight,
+                            const int64_t* slots, int32_t num_rows,
+                            int32_t kv_lora_rank, int32_t block_size,
+                            uint64_t cache_stride_bytes, float rms_eps,
+                            float inv_kv_scale, void* k_pool, void* stream);
+
 /* Thread-local message of the last failure on this thread ("" if none). */
 const char* dsa_decode_last_error(void);
 
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 300
+#define DSA_DECODE_VERSION 301
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "dsa_decode_plan", "dsa_decode_plan_destroy", "dsa_decode_workspace_bytes",
     "dsa_decode_workspace_init", "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
     "dsa_decode_timing_begin", "dsa_decode_timing_end", "dsa_decode_last_error",
-    "dsa_decode_version",
+    "dsa_decode_version", "dsa_decode_latent_write",
 )
 
 
@@ -122,6 +122,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_last_error.argtypes = []
         L.dsa_decode_version.restype = ctypes.c_int
         L.dsa_decode_version.argtypes = []
+        L.dsa_decode_latent_write.restype = ctypes.c_int
+        L.dsa_decode_latent_write.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_uint64,
+                                              ctypes.c_float, ctypes.c_float, vp, vp]
         _lib = L
     return _lib
 
@@ -280,3 +283,15 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
     finally:
         plan.close()
     return out
+
+
+def latent_write(kv_a, weight, slots, k_pool, *, block_size: int, rms_eps: float,
+                 inv_kv_scale: float, cache_stride_bytes: int = 0, stream=None) -> None:
+    """The cache writer: kv_a bf16 [N, D], weight bf16 [D], slots int64 [N]
+    (negative: skipped), k_pool the uint8 FP8 pool, all on the GPU. Writes
+    the FP8 rows in place; asynchronous on `stream`."""
+    n, d = kv_a.shape
+    _check(lib().dsa_decode_latent_write(
+        _ptr(kv_a), _ptr(weight), _ptr(slots), int(n), int(d), int(block_size),
+        int(cache_stride_bytes), float(rms_eps), float(inv_kv_scale), _ptr(k_pool),
+        _stream(stream)))

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(native):
 
 
 def test_version(native):
-    assert native.lib().dsa_decode_version() == 300
+    assert native.lib().dsa_decode_version() == 301
 
 
 def plan(native, **kw):
@@ -197,3 +197,34 @@ def test_binding_refuses_without_library(monkeypatch, native):
     monkeypatch.setattr(pkg, "library_path", lambda: "/nonexistent/libdsa_decode.so")
     with pytest.raises(RuntimeError, match="not built"):
         pkg.lib()
+
+
+# ------------------------------------------------------------ cache writer
+
+def _writer(native, **kw):
+    args = dict(kv_a=None, weight=None, slots=None, num_rows=0, kv_lora_rank=512,
+                block_size=64, cache_stride_bytes=0, rms_eps=1e-6, inv_kv_scale=50.0,
+                k_pool=None, stream=None)
+    args.update(kw)
+    return native.lib().dsa_decode_latent_write(*args.values())
+
+
+def test_writer_zero_rows_is_a_no_op(native):
+    assert _writer(native) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(kv_lora_rank=96), -2, "not compiled"),
+    (dict(block_size=0), -1, "block_size"),
+    (dict(cache_stride_bytes=64 * 512 - 16), -1, "cache_stride_bytes"),
+    (dict(cache_stride_bytes=64 * 512 + 8), -1, "cache_stride_bytes"),
+    (dict(rms_eps=-1.0), -1, "rms_eps"),
+    (dict(inv_kv_scale=0.0), -1, "inv_kv_scale"),
+    (dict(inv_kv_scale=float("inf")), -1, "inv_kv_scale"),
+    (dict(num_rows=-1), -1, "num_rows"),
+    (dict(num_rows=4), -1, "NULL"),
+    (dict(num_rows=4, kv_a=8, weight=16, slots=16, k_pool=16), -1, "aligned"),
+])
+def test_writer_rejects(native, kw, status, needle):
+    assert _writer(native, **kw) == status
+    assert needle in native.last_error()
