@@ -39,7 +39,10 @@ def parse():
     # load to settle (the first 200 launches run 10-20 % slower)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="long",
-                    choices=["glm", "long", "verify", "ragged"])
+                    choices=["glm", "long", "verify", "ragged", "latent_write"],
+                    help="decode workload, or latent_write: the cache writer alone")
+    ap.add_argument("--writer-rows", type=int, default=65536,
+                    help="latent_write: rows written per launch")
     ap.add_argument("--sets", type=int, default=4,
                     help="distinct input batches cycled through")
     ap.add_argument("--cpu-rows", type=int, default=128,
@@ -58,6 +61,10 @@ def main():
                           "runs on more than one GPU are not part of it (see DESIGN.md "
                           "for how it would shard)", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.workload == "latent_write":
+        bench_latent_write(args)
+        return
 
     import numpy as np
     import torch
@@ -114,16 +121,7 @@ def main():
     torch.cuda.synchronize()
 
     if args.calib_copy_mib:
-        # reference dispatch for counter calibration: reads and writes exactly
-        # calib bytes once each
-        n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+        calibration_copy(args.calib_copy_mib)
 
     # The timed region is K launches back to back on the launch stream,
     # bracketed by one pair of HIP events (a pair around every launch would
@@ -209,13 +207,26 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(workload):
+def calibration_copy(mib):
+    """Reference dispatch for counter calibration: reads and writes exactly
+    `mib` MiB once each."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+
+
+def measured_traffic(workload, kernel="dsa_decode_kernel", source="kernels.hip"):
     """HBM bytes per launch from the committed counter summary of this
-    workload, or None when there is none or the kernel source has changed
-    since the counters were taken."""
+    kernel and workload, or None when there is none or the kernel source has
+    changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"dsa_decode_kernel_{workload}_hbm_counters.json")
-    src = os.path.join(ROOT, "sparse_attention_decode_row_amd", "csrc", "kernels.hip")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
+    src = os.path.join(ROOT, "sparse_attention_decode_row_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -274,6 +285,150 @@ def cpu_baseline(wl, pool_dev, batch, nrows):
             "sample": f"{len(rows)} of {wl.rows} rows of the same workload (all "
                       f"{wl.heads} heads, {tokens} selected tokens), float64 C oracle, "
                       f"{dt:.2f} s wall"}
+
+
+def bench_latent_write(args):
+    """The cache writer alone: N bf16 kv_a rows of kv_lora_rank 512, RMSNorm
+    x weight / kv_scale, FP8 E4M3 into distinct random slots of a paged pool
+    (block_size 64). HBM-bound: per row it reads 2*D bytes and writes D bytes
+    (plus its 8-byte slot); the weight (2*D bytes) is read once per launch.
+    Input sets are cycled so that the bytes touched over a cycle exceed the
+    GPU's 256 MiB last-level cache."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_decode_row_amd as dsa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    D, B, N = 512, 64, args.writer_rows
+    eps, kv_scale = 1e-6, 0.02
+    per_set = N * (3 * D + 8)
+    sets = min(64, max(args.sets, math.ceil(512 * 2**20 / per_set)))
+    slots_total = sets * N
+    pages = (slots_total + B - 1) // B
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20240)
+    pool = torch.zeros(pages * B * D, dtype=torch.uint8, device=dev)
+    weight = (0.5 + torch.rand(D, generator=gen, device=dev)).to(torch.bfloat16)
+    # every set writes its own rows to its own slots: a random permutation of
+    # the pool's slots, dealt out N at a time
+    perm = torch.randperm(pages * B, generator=gen, device=dev)[:slots_total]
+    batches = []
+    for s in range(sets):
+        kv = torch.randn((N, D), generator=gen, device=dev).to(torch.bfloat16)
+        batches.append((kv, perm[s * N:(s + 1) * N].contiguous()))
+    stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+    print(f"[bench] latent_write: {N} rows x {D}, {sets} input sets, pool "
+          f"{pool.numel() / 2**20:.0f} MiB", file=sys.stderr, flush=True)
+
+    def step(i, n=N):
+        kv, sl = batches[i % sets]
+        dsa.latent_write(kv[:n], weight, sl[:n], pool, block_size=B, rms_eps=eps,
+                         inv_kv_scale=1.0 / kv_scale, stream=sptr)
+
+    def region(K, first, n=N):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ev0.record(stream)
+        for i in range(K):
+            step(first + i, n)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3, ev0.elapsed_time(ev1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.calib_copy_mib:
+        calibration_copy(args.calib_copy_mib)
+    K = args.steps
+    wall_ms, event_ms = region(K, args.warmup)
+    ms_per_step = wall_ms / K
+    kern_ms = event_ms / K
+    # one decode step's worth of new tokens (one per row of the long-context
+    # batch): launch-bound, reported beside the bulk figure
+    _, small_ms = region(K, 0, n=128)
+
+    alg = N * (3 * D + 8) + 2 * D
+    gbps = alg / (kern_ms / 1e3) / 1e9
+    result = {
+        "metric": "latent rows written to the FP8 paged cache per second",
+        "value": N / (ms_per_step / 1e3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"latent_write: {N} bf16 rows of kv_lora_rank {D} -> FP8 E4M3 "
+                        f"into random distinct slots of a {pool.numel() / 2**20:.0f} MiB "
+                        f"paged pool (block_size {B}), {sets} input sets cycled",
+            "rows": N, "kv_lora_rank": D, "block_size": B, "input_sets_cycled": sets,
+        },
+        "kernel_us": {"dsa_latent_write_kernel": kern_ms * 1e3},
+        "kernel_us_source": "HIP events around the timed region on the launch stream, / steps",
+        # back-to-back 128-row launches: bound by the host's launch rate, so
+        # this is an upper bound on the kernel's own duration at that size
+        "region_us_per_launch_128_rows": small_ms * 1e3 / K,
+        "arithmetic": "fp32 RMSNorm and scaling, hardware FP8 E4M3 conversion "
+                      "(nearest, ties to even) after saturating to +-448",
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "dsa_latent_write_kernel",
+            "achieved": gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gbps / HBM_PEAK_GBPS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg,
+        },
+    }
+    measured = measured_traffic("bulk", "dsa_latent_write_kernel", "latent_write.hip")
+    if measured is not None and N == 65536:
+        result["roofline"]["traffic"] = measured
+        result["roofline"]["traffic_unit"] = ("bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE "
+                                              "scaled by a 256 MiB copy's readings")
+    if args.cpu_rows > 0:
+        result["cpu_baseline"] = cpu_baseline_writer(batches[0], weight, B, eps, kv_scale,
+                                                     16 * args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_writer(batch, weight, block_size, eps, kv_scale, nrows):
+    """The CPU oracle's cache writer, as it stands (one thread), on the first
+    `nrows` rows of the first input set."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    kv, sl = batch
+    n = min(nrows, kv.shape[0])
+    kv_bits = kv[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+    w_bits = weight.view(torch.int16).cpu().numpy().view(np.uint16)
+    D = kv_bits.shape[1]
+    # the sample's rows go to slots 0..n-1 of a compact host pool
+    slots = np.arange(n, dtype=np.int64)
+    pool = np.zeros(((n + block_size - 1) // block_size) * block_size * D, dtype=np.uint8)
+    t = time.perf_counter()
+    oracle.latent_write(kv_bits, w_bits, slots, pool, block_size=block_size,
+                        cache_stride_bytes=0, eps=eps, inv_kv_scale=1.0 / kv_scale)
+    dt = time.perf_counter() - t
+    return {"value": n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {kv.shape[0]} rows of the first input set, float64 C "
+                      f"oracle, {dt:.2f} s wall"}
 
 
 if __name__ == "__main__":

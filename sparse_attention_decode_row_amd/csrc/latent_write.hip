@@ -4,10 +4,13 @@
 //
 // What is computed is defined on the page "metrale_model_arch/glm5next_dsa/
 // layer/decode_k.rs" (the latent_write launch and the slot of a position).
-// How: one wave per row, D/64 elements per lane (one 16-byte load of the row
-// and of the weight at D = 512), the sum of squares reduced across the wave
-// with DPP and cross-row swaps, the conversion on the hardware's FP8
-// converter after clamping to the largest finite value, one store per lane.
+// How: one wave per two rows, D/64 elements per lane (one 16-byte load per
+// row and one of the weight at D = 512); both rows' loads are issued before
+// either reduction, so each wave keeps 2 KiB in flight. The sum of squares is
+// reduced across the wave with DPP and cross-row swaps, the conversion runs on
+// the hardware's FP8 converter after clamping to the largest finite value,
+// one store per lane and row. kv_a rows are read once and pool rows written
+// once here, so both go through the nontemporal (streaming) cache policy.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -22,7 +25,8 @@ namespace {
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowsPerBlock = 4;  // one wave each
+constexpr int kWavesPerBlock = 4;
+constexpr int kRowsPerWave = 2;
 constexpr float kFp8Max = 448.0f;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -40,30 +44,31 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// E (1, 2, 4 or 8) consecutive bf16 values at p, as floats.
-template <int E>
-__device__ __forceinline__ void load_bf16(const uint16_t* p, float (&v)[E]) {
+// E (1, 2, 4 or 8) consecutive bf16 values at p, as raw 16-bit fields packed
+// in 32-bit words; NT: streaming load.
+template <int E, bool NT>
+__device__ __forceinline__ void load_raw(const uint16_t* p, uint32_t (&r)[(E + 1) / 2]) {
   if constexpr (E == 8) {
-    const u32x4 w = *(const u32x4*)p;
+    const u32x4* q = (const u32x4*)p;
+    const u32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
+    for (int i = 0; i < 4; ++i) r[i] = w[i];
   } else if constexpr (E == 4) {
-    const u32x2 w = *(const u32x2*)p;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
+    const u32x2* q = (const u32x2*)p;
+    const u32x2 w = NT ? __builtin_nontemporal_load(q) : *q;
+    r[0] = w[0];
+    r[1] = w[1];
   } else if constexpr (E == 2) {
-    const uint32_t w = *(const uint32_t*)p;
-    v[0] = bf16_to_f32(w & 0xffffu);
-    v[1] = bf16_to_f32(w >> 16);
+    const uint32_t* q = (const uint32_t*)p;
+    r[0] = NT ? __builtin_nontemporal_load(q) : *q;
   } else {
-    v[0] = bf16_to_f32(*p);
+    r[0] = NT ? __builtin_nontemporal_load(p) : *p;
   }
+}
+
+template <int E>
+__device__ __forceinline__ float raw_elem(const uint32_t (&r)[(E + 1) / 2], int i) {
+  return bf16_to_f32((i & 1) ? (r[i >> 1] >> 16) : (r[i >> 1] & 0xffffu));
 }
 
 // Four floats -> four FP8 E4M3FN codes (nearest, ties to even), byte i = x_i;
@@ -74,47 +79,73 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
 }
 
 template <int D>
-__global__ __launch_bounds__(kRowsPerBlock * 64)
+__global__ __launch_bounds__(kWavesPerBlock * 64)
 void dsa_latent_write_kernel(const uint16_t* kv_a, const uint16_t* weight,
                              const int64_t* slots, int rows, int block_size,
                              uint64_t stride, float eps, float inv_kv_scale,
                              uint8_t* pool) {
   constexpr int E = D / 64;
+  constexpr int W = (E + 1) / 2;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerBlock + (int)(threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int64_t slot = slots[row];
-  if (slot < 0) return;  // no slot: nothing is written
-
-  float x[E], w[E];
-  load_bf16<E>(kv_a + (size_t)row * D + lane * E, x);
-  load_bf16<E>(weight + lane * E, w);
-  float ss = 0.f;
+  const int row0 = (blockIdx.x * kWavesPerBlock + (int)(threadIdx.x >> 6)) * kRowsPerWave;
+  int64_t slot[kRowsPerWave];
 #pragma unroll
-  for (int i = 0; i < E; ++i) ss = fmaf(x[i], x[i], ss);
-  ss = wave_sum(ss);
-  const float inv_rms = 1.0f / sqrtf(ss * (1.0f / D) + eps);
-
-  float y[E < 4 ? 4 : E];
+  for (int j = 0; j < kRowsPerWave; ++j) slot[j] = row0 + j < rows ? slots[row0 + j] : -1;
+  // a negative slot (or a row past the end) writes nothing; the row itself is
+  // loaded whenever it exists, so that its load does not wait for the slot's
+  uint32_t raw[kRowsPerWave][W];
 #pragma unroll
-  for (int i = 0; i < (E < 4 ? 4 : E); ++i) y[i] = 0.f;
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    if (row0 + j < rows) {
+      load_raw<E, true>(kv_a + (size_t)(row0 + j) * D + lane * E, raw[j]);
+    } else {
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const float v = x[i] * inv_rms * w[i] * inv_kv_scale;
-    y[i] = fminf(fmaxf(v, -kFp8Max), kFp8Max);  // saturate (never NaN)
+      for (int i = 0; i < W; ++i) raw[j][i] = 0u;
+    }
   }
-  const int64_t page = slot / block_size;
-  const int64_t in_page = slot - page * block_size;
-  uint8_t* dst = pool + (uint64_t)page * stride + (uint64_t)in_page * D + lane * E;
-  if constexpr (E == 8) {
-    const u32x2 c = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
-    *(u32x2*)dst = c;
-  } else if constexpr (E == 4) {
-    *(uint32_t*)dst = pack_fp8x4(y[0], y[1], y[2], y[3]);
-  } else if constexpr (E == 2) {
-    *(uint16_t*)dst = (uint16_t)(pack_fp8x4(y[0], y[1], 0.f, 0.f) & 0xffffu);
-  } else {
-    *dst = (uint8_t)(pack_fp8x4(y[0], 0.f, 0.f, 0.f) & 0xffu);
+  uint32_t wraw[W];
+  load_raw<E, false>(weight + lane * E, wraw);
+
+  float ss[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float x = raw_elem<E>(raw[j], i);
+      acc = fmaf(x, x, acc);
+    }
+    ss[j] = acc;
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) ss[j] = wave_sum(ss[j]);
+
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    if (slot[j] < 0) continue;
+    const float inv_rms = 1.0f / sqrtf(ss[j] * (1.0f / D) + eps);
+    float y[E < 4 ? 4 : E];
+#pragma unroll
+    for (int i = 0; i < (E < 4 ? 4 : E); ++i) y[i] = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float v = raw_elem<E>(raw[j], i) * inv_rms * raw_elem<E>(wraw, i) * inv_kv_scale;
+      y[i] = fminf(fmaxf(v, -kFp8Max), kFp8Max);  // saturate (never NaN)
+    }
+    const int64_t page = slot[j] / block_size;
+    const int64_t in_page = slot[j] - page * block_size;
+    uint8_t* dst = pool + (uint64_t)page * stride + (uint64_t)in_page * D + lane * E;
+    if constexpr (E == 8) {
+      const u32x2 c = {pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7])};
+      __builtin_nontemporal_store(c, (u32x2*)dst);
+    } else if constexpr (E == 4) {
+      __builtin_nontemporal_store(pack_fp8x4(y[0], y[1], y[2], y[3]), (uint32_t*)dst);
+    } else if constexpr (E == 2) {
+      __builtin_nontemporal_store((uint16_t)(pack_fp8x4(y[0], y[1], 0.f, 0.f) & 0xffffu),
+                                  (uint16_t*)dst);
+    } else {
+      __builtin_nontemporal_store((uint8_t)(pack_fp8x4(y[0], 0.f, 0.f, 0.f) & 0xffu), dst);
+    }
   }
 }
 
@@ -122,7 +153,8 @@ template <int D>
 hipError_t launch_writer(const void* kv_a, const void* weight, const int64_t* slots, int rows,
                          int block_size, uint64_t stride, float eps, float inv, void* pool,
                          hipStream_t st) {
-  const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(kRowsPerBlock * 64);
+  constexpr int kRowsPerBlock = kWavesPerBlock * kRowsPerWave;
+  const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(kWavesPerBlock * 64);
   hipLaunchKernelGGL((dsa_latent_write_kernel<D>), grid, block, 0, st, (const uint16_t*)kv_a,
                      (const uint16_t*)weight, slots, rows, block_size, stride, eps, inv,
                      (uint8_t*)pool);

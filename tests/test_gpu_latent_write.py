@@ -103,6 +103,18 @@ def test_writer_matches_oracle(H, D, B, pad):
     assert ties <= max(2, n // 1000)
 
 
+@pytest.mark.parametrize("rows,D", [(1, 512), (2, 512), (7, 512), (8, 512), (9, 512),
+                                    (3, 64), (5, 256)])
+def test_writer_small_batches(H, rows, D):
+    """Batches that leave waves and workgroups partly filled (two rows per
+    wave, eight per workgroup)."""
+    rng = np.random.default_rng(400 + rows + D)
+    _announce("latent_write small", rows=rows, D=D)
+    ties, n, *_ = _run_case(H, rng, rows=rows, D=D, B=16, pages=4, stride_pad=0,
+                            sigma=2.0, inv=1 / 0.05, neg_slots=1 if rows >= 7 else 0)
+    assert ties <= 2
+
+
 def test_writer_saturates(H):
     rng = np.random.default_rng(9)
     _announce("latent_write saturation")
