@@ -51,6 +51,9 @@ def parse():
                     help="also run one plain device copy of this many MiB "
                          "(reference dispatch for HBM counter calibration)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--rows-per-sequence", type=int, default=-1,
+                    help="decode_k rows per sequence co-scheduled on one XCD "
+                         "(-1: the workload's own, 4 for verify, else 1)")
     return ap.parse_args()
 
 
@@ -98,11 +101,15 @@ def main():
             n += int(np.unique(row[(row >= 0) & (row < wl.seq_lens[r])]).size)
         uniq_per_step.append(n)
     out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
+    # the verify workload holds 4 consecutive decode_k rows per sequence
+    rows_per_seq = (args.rows_per_sequence if args.rows_per_sequence >= 0
+                    else (4 if name == "verify" else 1))
     plan = dsa.Plan(num_rows=R, num_q_heads=H, kv_lora_rank=D,
                     block_size=base.block_size, index_kpool=base.kpool, sel_width=W,
                     block_table_stride=base.bt_stride, max_seq_len=base.max_seq_len,
                     sm_scale=base.sm_scale, cache_stride_bytes=base.cache_stride_bytes,
-                    chunk_tokens=args.chunk_tokens, device=0)
+                    chunk_tokens=args.chunk_tokens,
+                    rows_per_sequence=rows_per_seq, device=0)
     ws = plan.new_workspace(0)
     info = plan.info()
     stream = torch.cuda.current_stream()

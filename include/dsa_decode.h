@@ -94,7 +94,17 @@ typedef struct dsa_decode_params {
    * The head blocks of a row read the same latent rows through the same L2.
    * The result does not depend on it. */
   int32_t layout;
-  int32_t reserved[3]; /* must be zero */
+  /* 0 or 1: rows are scheduled independently. k > 1: rows s*k .. s*k + k - 1
+   * are the k consecutive query rows of one sequence in a k-token decode
+   * step ([decode_k]: k rows per sequence at positions pos .. pos + k - 1,
+   * each with its own selection and seq_len, all reading the sequence's
+   * block-table row), so their selections overlap. The planner puts the
+   * workgroups of those k rows on one XCD in the same dispatch round, so
+   * the latent rows their selections share are fetched from HBM about once
+   * and served to the others by that XCD's L2. num_rows must be a multiple
+   * of k. The result does not depend on it. */
+  int32_t rows_per_sequence;
+  int32_t reserved[2]; /* must be zero */
 } dsa_decode_params;
 
 #define DSA_DECODE_LAYOUT_AUTO 0
@@ -112,7 +122,8 @@ typedef struct dsa_decode_plan_info {
   int32_t chunks_per_row;  /* workgroups per row per head block */
   int32_t head_blocks;     /* groups of up to heads_per_block heads */
   int32_t workgroups;      /* launched: rows * chunks_per_row rounded up to
-                            * a multiple of 8, times head_blocks */
+                            * a multiple of 8 (of 8 * rows_per_sequence when
+                            * rows are co-scheduled), times head_blocks */
   int32_t merges_chunks;   /* 1 when chunks_per_row > 1: the last chunk of a
                             * row to finish merges the others' partials */
   int32_t num_cus;         /* compute units the plan was sized for */
@@ -122,6 +133,7 @@ typedef struct dsa_decode_plan_info {
   uint64_t workspace_bytes;
   int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32 or _HEADS16 (resolved) */
   int32_t heads_per_block; /* 32 or 16 */
+  int32_t rows_per_sequence; /* rows co-scheduled on one XCD (1: none) */
 } dsa_decode_plan_info;
 
 /* Validate params and build a plan.
@@ -245,7 +257,7 @@ const char* dsa_decode_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 301
+#define DSA_DECODE_VERSION 302
 
 #ifdef __cplusplus
 }

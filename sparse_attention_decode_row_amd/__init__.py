@@ -61,7 +61,8 @@ class Params(ctypes.Structure):
         ("sm_scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32),
         ("layout", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("rows_per_sequence", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -78,6 +79,7 @@ class PlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_uint64),
         ("layout", ctypes.c_int32),
         ("heads_per_block", ctypes.c_int32),
+        ("rows_per_sequence", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:
@@ -164,7 +166,8 @@ class Plan:
                  block_size: int, index_kpool: int, sel_width: int,
                  block_table_stride: int, max_seq_len: int, sm_scale: float,
                  num_kv_heads: int = 1, cache_stride_bytes: int = 0,
-                 chunk_tokens: int = 0, layout: int = 0, device: Optional[int] = None):
+                 chunk_tokens: int = 0, layout: int = 0, rows_per_sequence: int = 0,
+                 device: Optional[int] = None):
         if device is None:
             import torch
             device = torch.cuda.current_device()
@@ -172,7 +175,7 @@ class Plan:
         self.params = Params(num_rows, num_q_heads, num_kv_heads, kv_lora_rank,
                              block_size, index_kpool, sel_width, block_table_stride,
                              cache_stride_bytes, max_seq_len, sm_scale, chunk_tokens,
-                             layout, (ctypes.c_int32 * 3)(0, 0, 0))
+                             layout, rows_per_sequence, (ctypes.c_int32 * 2)(0, 0))
         h = ctypes.c_void_p()
         _check(self._lib.dsa_decode_plan(ctypes.byref(self.params), int(device),
                                          ctypes.byref(h)))

@@ -261,6 +261,7 @@ struct DecodeArgs {
   int head_blocks;
   int heads_per_block;  // 16 * kGroups
   int rows_hb;       // R * head_blocks (stride between the two counter arrays)
+  int group_units;   // (row, chunk) units co-scheduled on one XCD (1: none)
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
 };
@@ -335,10 +336,17 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Workgroup -> (row, chunk, head block). The head blocks of one (row,
   // chunk) read the same latent rows, so they get ids 8 apart: the same XCD
   // (ids are dealt to the 8 XCDs round-robin) and its L2 serves the second
-  // read.
+  // read. Ids come in rounds of 8 (one per XCD) per head block. When the
+  // rows of a sequence are co-scheduled, its group_units (row, chunk) units
+  // take group_units consecutive rounds on one XCD, for the same reason.
   const int bid = blockIdx.x;
   const int hb = (bid >> 3) % a.head_blocks;
-  const int rc = (bid / (8 * a.head_blocks)) * 8 + (bid & 7);
+  int rc = (bid / (8 * a.head_blocks)) * 8 + (bid & 7);
+  if (a.group_units > 1) {
+    const int round = rc >> 3, xcd = rc & 7;
+    const int blk = round / a.group_units, i = round - blk * a.group_units;
+    rc = (blk * 8 + xcd) * a.group_units + i;
+  }
   if (rc >= a.rows * a.chunks) return;  // grid padding
   const int r = rc / a.chunks, c = rc % a.chunks;
 
@@ -1220,6 +1228,7 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.head_blocks = plan->head_blocks;
   da.heads_per_block = plan->heads_per_block;
   da.rows_hb = p.num_rows * plan->head_blocks;
+  da.group_units = plan->group_units;
   da.scale_log2 = p.sm_scale * k_scale * kLog2e;
   da.v_scale = v_scale;
   const int groups = plan->heads_per_block / 16;

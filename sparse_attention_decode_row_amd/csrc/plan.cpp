@@ -125,7 +125,13 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
       << kMaxChunkTokens;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  for (int i = 0; i < 3; ++i)
+  if (p->rows_per_sequence < 0 ||
+      (p->rows_per_sequence > 1 && p->num_rows % p->rows_per_sequence != 0)) {
+    m << "dsa_decode_plan: rows_per_sequence " << p->rows_per_sequence
+      << " must be 0, 1, or a k > 1 that divides num_rows " << p->num_rows;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  for (int i = 0; i < 2; ++i)
     if (p->reserved[i] != 0)
       return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
   if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS16) {
@@ -211,7 +217,17 @@ void plan_layout(dsa_decode_plan_s* plan) {
   L.total = off;
   // Workgroup ids: the head blocks of one (row, chunk) are 8 apart, so the
   // (row, chunk) count is padded to a multiple of 8 (padding ids exit).
-  plan->workgroups = (int)((R * plan->chunks + 7) / 8 * 8 * plan->head_blocks);
+  // Co-scheduled sequences: the rows_per_sequence x chunks units of one
+  // sequence take consecutive rounds of 8 ids on one XCD, 8 sequences per
+  // block of rounds, so the unit count is padded to whole blocks.
+  const int64_t k = p.rows_per_sequence > 1 ? p.rows_per_sequence : 1;
+  plan->group_units = k > 1 ? (int)(k * plan->chunks) : 1;
+  if (k > 1) {
+    const int64_t seqs = R / k;
+    plan->workgroups = (int)((seqs + 7) / 8 * 8 * plan->group_units * plan->head_blocks);
+  } else {
+    plan->workgroups = (int)((R * plan->chunks + 7) / 8 * 8 * plan->head_blocks);
+  }
 }
 
 }  // namespace dsa
@@ -288,6 +304,7 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->chunk_lead = plan->chunk_lead;
   info->layout = plan->layout;
   info->heads_per_block = plan->heads_per_block;
+  info->rows_per_sequence = plan->p.rows_per_sequence > 1 ? plan->p.rows_per_sequence : 1;
   info->workspace_bytes = plan->ws.total;
   return DSA_DECODE_OK;
 }

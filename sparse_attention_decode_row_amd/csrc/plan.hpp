@@ -46,6 +46,7 @@ struct dsa_decode_plan_s {
   int heads_per_block = dsa::kHeadsPerBlock;
   int layout = DSA_DECODE_LAYOUT_HEADS32;
   int workgroups = 0;             // launched grid (rows x chunks padded to 8, x head blocks)
+  int group_units = 1;            // (row, chunk) units co-scheduled on one XCD: rows_per_sequence x chunks, or 1
   dsa::WorkspaceLayout ws;
   // benchmark timing (dsa_decode_timing_begin / _end)
   std::vector<void*> events;      // hipEvent_t, 2 per recorded launch

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(native):
 
 
 def test_version(native):
-    assert native.lib().dsa_decode_version() == 301
+    assert native.lib().dsa_decode_version() == 302
 
 
 def plan(native, **kw):
@@ -69,6 +69,8 @@ def plan(native, **kw):
     (dict(sm_scale=float("inf")), -1, "sm_scale must be finite"),
     (dict(chunk_tokens=100), -1, "chunk_tokens"),
     (dict(chunk_tokens=4096), -1, "chunk_tokens"),
+    (dict(rows_per_sequence=-1), -1, "rows_per_sequence"),
+    (dict(num_rows=10, rows_per_sequence=4), -1, "divides num_rows 10"),
 ])
 def test_plan_rejects(native, kw, status, needle):
     with pytest.raises(native.DsaDecodeError) as e:
@@ -228,3 +230,49 @@ def test_writer_zero_rows_is_a_no_op(native):
 def test_writer_rejects(native, kw, status, needle):
     assert _writer(native, **kw) == status
     assert needle in native.last_error()
+
+
+def test_rows_per_sequence_grid(native):
+    """Co-scheduled decode_k rows: the grid covers whole blocks of 8
+    sequences, each sequence's rows x chunks units in consecutive rounds."""
+    base = dict(num_rows=256, max_seq_len=32768, block_table_stride=512, layout=1)
+    plain = plan(native, **base).info()
+    assert plain["rows_per_sequence"] == 1
+    grouped = plan(native, rows_per_sequence=4, **base).info()
+    assert grouped["rows_per_sequence"] == 4
+    # 64 sequences fill 8 blocks exactly: the same grid as without grouping
+    assert grouped["workgroups"] == plain["workgroups"]
+    assert grouped["chunks_per_row"] == plain["chunks_per_row"]
+    assert grouped["workspace_bytes"] == plain["workspace_bytes"]
+    # 5 sequences of 3 rows: one block of 8 sequences, padded
+    odd = plan(native, num_rows=15, rows_per_sequence=3, max_seq_len=32768,
+               block_table_stride=512, layout=1).info()
+    assert odd["workgroups"] == 8 * 3 * odd["chunks_per_row"] * odd["head_blocks"]
+    assert plan(native, rows_per_sequence=1, **base).info()["workgroups"] == plain["workgroups"]
+
+
+def test_rows_per_sequence_mapping_is_a_bijection():
+    """The kernel's workgroup -> (row, chunk) map for co-scheduled rows,
+    restated here: every unit is hit exactly once, the units of a sequence
+    share an XCD (id mod 8) and head blocks of one unit are 8 ids apart."""
+    for seqs, k, chunks, hb in [(64, 4, 1, 2), (5, 3, 2, 1), (9, 2, 3, 4), (1, 5, 1, 1)]:
+        G = k * chunks
+        blocks = -(-seqs // 8)
+        grid = blocks * 8 * G * hb
+        seen = {}
+        for bid in range(grid):
+            h = (bid >> 3) % hb
+            lin = (bid // (8 * hb)) * 8 + (bid & 7)
+            rnd, x = lin >> 3, lin & 7
+            blk, i = divmod(rnd, G)
+            rc = (blk * 8 + x) * G + i
+            if rc >= seqs * k * chunks:
+                continue
+            assert (rc, h) not in seen
+            seen[(rc, h)] = bid
+        assert len(seen) == seqs * k * chunks * hb
+        for (rc, h), bid in seen.items():
+            s = rc // G
+            assert bid % 8 == s % 8
+            if h > 0:
+                assert seen[(rc, h - 1)] == bid - 8

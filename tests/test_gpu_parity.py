@@ -89,6 +89,48 @@ def test_verify_sampled_rows(H):
     assert err.max() <= H.TOL
 
 
+def test_verify_rows_co_scheduled_per_sequence(H):
+    """decode_k rows of one sequence co-scheduled on one XCD
+    (rows_per_sequence = 4): bit-identical to independent scheduling, and
+    the sampled rows match the oracle."""
+    wl = WL.make("verify", with_pool=False)
+    _announce("verify co-scheduled", rows=wl.rows, rows_per_sequence=4)
+    pool = WL.device_pool(wl.num_pages, wl.block_size, wl.D, wl.sigma, wl.k_scale,
+                          seed=wl.seed)
+    base = H.run_gpu(wl, k_pool=pool)
+    run = H.run_gpu(wl, k_pool=pool, rows_per_sequence=4)
+    print("plan", run.info)
+    assert run.info["rows_per_sequence"] == 4
+    H.check_selection(wl, run)
+    assert np.array_equal(run.out_bits, base.out_bits)
+    rows = [0, 3, 4, 130, 255]
+    sub, view = H.sub_pool_for_rows(wl, pool, rows)
+    want = H.oracle_rows(view, rows, host_pool=sub)
+    err = H.normwise_err(run.out[rows], want)
+    print(f"verify co-scheduled rows {rows} max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+
+
+@pytest.mark.parametrize("k,chunk_tokens", [(3, 64), (5, 0)])
+def test_co_scheduled_rows_with_padding_and_splits(H, k, chunk_tokens):
+    """A sequence count that leaves a block of 8 partly empty, with and
+    without split chunks: same bits as independent scheduling, oracle parity
+    on every row."""
+    rng = np.random.default_rng(77 + k)
+    seqs = 5
+    wl = WL.random_case(rng, rows=seqs * k, heads=40, D=128, block_size=16,
+                        width=300, max_len=900)
+    _announce("co-scheduled", rows=wl.rows, k=k, chunk_tokens=chunk_tokens)
+    base = H.run_gpu(wl, chunk_tokens=chunk_tokens)
+    run = H.run_gpu(wl, chunk_tokens=chunk_tokens, rows_per_sequence=k)
+    H.check_selection(wl, run)
+    assert np.array_equal(run.out_bits, base.out_bits)
+    want = H.oracle_rows(wl, range(wl.rows))
+    err = H.normwise_err(run.out, want)
+    print(f"co-scheduled k={k} max err {err.max():.3e} plan {run.info}")
+    assert err.max() <= H.TOL
+
+
 def test_ragged_all_rows(H):
     wl = WL.make("ragged", with_pool=False)
     _announce("ragged", rows=wl.rows, heads=wl.heads, pages=wl.num_pages)
