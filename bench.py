@@ -204,7 +204,7 @@ def main():
                  "fp8_issued_flops_per_launch": 2 * flops, "fp8_peak": 5000.0},
     }
 
-    measured = measured_traffic(name)
+    measured = measured_traffic(name, rows_per_sequence=rows_per_seq)
     if measured is not None:
         result["roofline"]["traffic"] = measured
         result["roofline"]["traffic_unit"] = ("bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE "
@@ -227,10 +227,12 @@ def calibration_copy(mib):
     print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload, kernel="dsa_decode_kernel", source="kernels.hip"):
+def measured_traffic(workload, kernel="dsa_decode_kernel", source="kernels.hip",
+                     rows_per_sequence=None):
     """HBM bytes per launch from the committed counter summary of this
-    kernel and workload, or None when there is none or the kernel source has
-    changed since the counters were taken."""
+    kernel and workload, or None when there is none, the kernel source has
+    changed since the counters were taken, or they were taken with another
+    rows_per_sequence."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.json")
     src = os.path.join(ROOT, "sparse_attention_decode_row_amd", "csrc", source)
@@ -241,6 +243,8 @@ def measured_traffic(workload, kernel="dsa_decode_kernel", source="kernels.hip")
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     if rec.get("kernel_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    if rows_per_sequence is not None and rec.get("rows_per_sequence", 1) != rows_per_sequence:
         return None
     return float(rec["traffic_bytes_per_launch"])
 
