@@ -251,6 +251,32 @@ int dsa_decode_latent_write(const void* kv_a, const void* weight,
                             uint64_t cache_stride_bytes, float rms_eps,
                             float inv_kv_scale, void* k_pool, void* stream);
 
+/* Dense masked-attention reference of the decode, for cross-checking it on
+ * the GPU at full size ([attend] module doc, "Why this is not the masked
+ * kernel": the selected-index decode equals attention over every position
+ * t < seq_lens[r] with a mask keeping exactly the selected positions).
+ * Plain fp32, one workgroup per (row, head), untuned and separate from the
+ * decode kernel. For each row r and head h:
+ *   S = { t in [0, L) : t appears in sel_indices[r, :] },
+ *       L = min(max(seq_lens[r], 0), max_seq_len)
+ *   s_t = sm_scale * k_scale * sum_d q[r,h,d] * fp8(k row of t)[d]
+ *   out[r,h,d] = v_scale * sum_t exp(s_t - max s) * fp8(v row of t)[d]
+ *                / sum_t exp(s_t - max s),      t in S ascending
+ * and out[r,h,:] = 0 when S is empty. Geometry, buffers and addressing are
+ * those of dsa_decode_launch (params as for dsa_decode_plan; q bf16
+ * [R, H, D], pools FP8 E4M3FN, block_tables, seq_lens, sel_indices int32),
+ * except that out is float32 [R, H, D]. Runs on the current HIP device,
+ * which must be gfx950, enqueued on `stream` (NULL = default); allocates
+ * and retains nothing. Errors: DSA_DECODE_ERR_INVALID (params, a NULL
+ * buffer, non-finite scales, or 4 * ceil(max_seq_len / 32) + 8 * sel_width
+ * bytes of LDS above 159 KiB), DSA_DECODE_ERR_UNSUPPORTED, _DEVICE, _LAUNCH.
+ * Device-side preconditions as for dsa_decode_launch. */
+int dsa_decode_masked_reference(const dsa_decode_params* params, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* sel_indices, float k_scale, float v_scale,
+                         float* out, void* stream);
+
 /* Thread-local message of the last failure on this thread ("" if none). */
 const char* dsa_decode_last_error(void);
 

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = (
     "dsa_decode_plan", "dsa_decode_plan_destroy", "dsa_decode_workspace_bytes",
     "dsa_decode_workspace_init", "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
     "dsa_decode_timing_begin", "dsa_decode_timing_end", "dsa_decode_last_error",
-    "dsa_decode_version", "dsa_decode_latent_write",
+    "dsa_decode_version", "dsa_decode_latent_write", "dsa_decode_masked_reference",
 )
 
 
@@ -127,6 +127,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_latent_write.restype = ctypes.c_int
         L.dsa_decode_latent_write.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_uint64,
                                               ctypes.c_float, ctypes.c_float, vp, vp]
+        L.dsa_decode_masked_reference.restype = ctypes.c_int
+        L.dsa_decode_masked_reference.argtypes = [ctypes.POINTER(Params), vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_float, ctypes.c_float, vp, vp]
         _lib = L
     return _lib
 
@@ -298,3 +301,24 @@ def latent_write(kv_a, weight, slots, k_pool, *, block_size: int, rms_eps: float
         _ptr(kv_a), _ptr(weight), _ptr(slots), int(n), int(d), int(block_size),
         int(cache_stride_bytes), float(rms_eps), float(inv_kv_scale), _ptr(k_pool),
         _stream(stream)))
+
+
+def masked_reference(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
+                     k_scale: float, v_scale: float, block_size: int, index_kpool: int,
+                     block_table_stride: int, max_seq_len: int, sm_scale: float,
+                     cache_stride_bytes: int = 0, out=None, stream=None):
+    """Dense masked-attention reference of the decode on the GPU
+    (dsa_decode_masked_reference): plain fp32, one workgroup per (row, head). Same
+    inputs as decode(); returns out, float32 [R, H, D]."""
+    import torch
+    R, H, D = q.shape
+    params = Params(R, H, 1, D, block_size, index_kpool, sel_indices.shape[1],
+                    block_table_stride, cache_stride_bytes, max_seq_len, sm_scale, 0, 0, 0,
+                    (ctypes.c_int32 * 2)(0, 0))
+    if out is None:
+        out = torch.empty((R, H, D), dtype=torch.float32, device=q.device)
+    _check(lib().dsa_decode_masked_reference(
+        ctypes.byref(params), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(seq_lens), _ptr(sel_indices), float(k_scale), float(v_scale), _ptr(out),
+        _stream(stream)))
+    return out

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdsa_decode.so")
 SOURCES = [os.path.join(HERE, "csrc", "plan.cpp"),
            os.path.join(HERE, "csrc", "kernels.hip"),
-           os.path.join(HERE, "csrc", "latent_write.hip")]
+           os.path.join(HERE, "csrc", "latent_write.hip"),
+           os.path.join(HERE, "csrc", "masked_reference.hip")]
 HEADERS = [os.path.join(ROOT, "include", "dsa_decode.h"),
            os.path.join(HERE, "csrc", "plan.hpp")]
 

@@ -276,3 +276,41 @@ def test_rows_per_sequence_mapping_is_a_bijection():
             assert bid % 8 == s % 8
             if h > 0:
                 assert seen[(rc, h - 1)] == bid - 8
+
+
+def _reference_call(native, *, rows=2, heads=4, D=64, width=8, **kw):
+    """The masked reference with host tensors standing in for device buffers:
+    every check these cases reach runs before anything is read."""
+    import torch
+    args = dict(k_scale=0.05, v_scale=0.05, block_size=16, index_kpool=4,
+                block_table_stride=16, max_seq_len=256, sm_scale=0.125)
+    args.update(kw)
+    q = torch.zeros((rows, heads, D), dtype=torch.bfloat16)
+    pool = torch.zeros(64, dtype=torch.uint8)
+    bt = torch.zeros((rows, 16), dtype=torch.int32)
+    sl = torch.zeros(rows, dtype=torch.int32)
+    sel = torch.zeros((rows, width), dtype=torch.int32)
+    out = torch.zeros((rows, heads, D), dtype=torch.float32)
+    return native.masked_reference(q, pool, pool, bt, sl, sel, out=out, stream=0, **args)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(block_size=0), -1, "block_size must be > 0"),
+    (dict(D=576), -2, "not compiled in"),
+    (dict(k_scale=float("nan")), -1, "k_scale and v_scale must be finite"),
+    (dict(max_seq_len=1 << 22, block_table_stride=1 << 18, width=2048), -1, "bytes of LDS"),
+])
+def test_masked_reference_rejects(native, kw, status, needle):
+    with pytest.raises(native.DsaDecodeError) as e:
+        _reference_call(native, **kw)
+    assert e.value.status == status
+    assert needle in str(e.value)
+
+
+def test_masked_reference_without_gpu_is_a_device_error(native):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(native.DsaDecodeError) as e:
+        _reference_call(native)
+    assert e.value.status == native.DSA_DECODE_ERR_DEVICE
