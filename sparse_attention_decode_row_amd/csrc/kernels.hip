@@ -167,6 +167,20 @@ __device__ __forceinline__ void store_dev16(float* p, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
+// Device-scope (coherent) loads of what other workgroups published with
+// device-scope stores: they read past any stale copy in this CU's or this
+// XCD's caches, so the reader needs no cache invalidation.
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_dev16(const float* p) {
+  uint64_t* q = (uint64_t*)const_cast<float*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+               __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+}
+
 // Maximum of two values that are never NaN, as one median-of-three against
 // +inf: the compiler's maximum first quiets each operand (one more
 // instruction apiece). The +inf is passed in a register the compiler cannot
@@ -968,8 +982,11 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Split chunks. Each workgroup counts itself in; the last one to arrive
   // merges. The others publish their partials (each PV wave's accumulators
   // as they sit in its registers, 1 KiB per store, then (reference, sum) of
-  // the block's heads), written through device-coherently, and count them
-  // published; the merger waits for that count. Only workgroups that have
+  // the block's heads) with device-scope stores, wait for those stores to
+  // complete, and only then count themselves published: the stores are
+  // visible at device scope without a cache write-back. The merger waits for
+  // that count and reads the partials with device-scope loads, so no cache
+  // is written back or invalidated on either side. Only workgroups that have
   // already arrived are waited for, so the wait always ends; a bounded spin
   // turns a broken count into NaN output instead of a hang.
   constexpr int kPartFloats = kGroups * kCB * kWave * 4;  // per PV wave
@@ -977,8 +994,8 @@ void dsa_decode_kernel(DecodeArgs a) {
   const int rh = r * a.head_blocks + hb;
   int32_t* arrived = a.ws_arrivals + rh;
   int32_t* published = a.ws_arrivals + (size_t)a.rows_hb + rh;
-  auto part_o_of = [&](int cc) {
-    return a.part_o + ((wg_slot + cc) * kPVWaves + pw) * kPartFloats;
+  auto part_o_of = [&](int cc, int src) {
+    return a.part_o + ((wg_slot + cc) * kPVWaves + src) * kPartFloats;
   };
   auto part_ml_of = [&](int cc, int x) {
     return a.part_ml + ((wg_slot + cc) * a.heads_per_block + x * 16 + li) * 2;
@@ -987,7 +1004,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (flag_sh != 2) {
     if (!is_qk) {
-      float* po = part_o_of(c);
+      float* po = part_o_of(c, pw);
 #pragma unroll
       for (int x = 0; x < kGroups; ++x)
 #pragma unroll
@@ -1002,12 +1019,19 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
     wait_vmcnt<0>();  // this wave's stores are complete before the barrier
     __syncthreads();
-    if (tid == 0) {
-      __threadfence();
-      atomicAdd(published, 1);
-    }
+    if (tid == 0) atomicAdd(published, 1);
     return;
   }
+  // The merger: the PV waves stage their own chunk's accumulators in LDS
+  // (same layout as a published partial) while thread 0 waits for the
+  // others; then every wave merges an equal share of the block's output.
+  f32x4* own = (f32x4*)smem;  // [PV wave][group][column block][lane]
+  static_assert(kPVWaves * kGroups * kCB * kWave * 16 <= kSmemBytes, "merge staging area");
+  if (!is_qk)
+#pragma unroll
+    for (int x = 0; x < kGroups; ++x)
+#pragma unroll
+      for (int j = 0; j < kCB; ++j) own[((pw * kGroups + x) * kCB + j) * kWave + lane] = O[x][j];
   if (tid == 0) {
     constexpr int kMaxSpins = 1 << 24;
     int spins = 0;
@@ -1022,62 +1046,88 @@ void dsa_decode_kernel(DecodeArgs a) {
     // next launch
     __hip_atomic_store(arrived, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
   }
   __syncthreads();
-  if (is_qk) return;
   const float poison = flag_sh == 2 ? 0.f : __builtin_nanf("");
-  // Online log-sum-exp merge in fixed chunk order (deterministic whichever
-  // chunk merges); each chunk's (reference, sum, partial) loads are issued
-  // together.
+  // Wave w merges units (group x, column block j) half*kU .. half*kU + kU - 1
+  // of PV wave src = w % kPVWaves's register order (unit = x * kCB + j).
+  constexpr int kU = kGroups * kCB / 2;
+  static_assert(kU >= 1 && 2 * kU == kGroups * kCB && 2 * kPVWaves == kWaves, "merge split");
+  const int src = wave % kPVWaves, half = wave / kPVWaves;
+  auto unit_x = [&](int u) { return (half * kU + u) / kCB; };
+  auto unit_j = [&](int u) { return (half * kU + u) % kCB; };
+  // Per group: the largest reference over the chunks, each chunk's weight
+  // 2^(m_c - M) and the total sum, in fixed chunk order (deterministic
+  // whichever chunk merges).
   float M[kGroups], Ls[kGroups];
-  f32x4 acc[kGroups][kCB];
 #pragma unroll
-  for (int x = 0; x < kGroups; ++x) {
-    M[x] = -INFINITY;
-    Ls[x] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kCB; ++j) acc[x][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int x = 0; x < kGroups; ++x) M[x] = m_run[x];
   for (int cc = 0; cc < a.chunks; ++cc) {
-    float mc[kGroups], lc[kGroups];
-    f32x4 oc[kGroups][kCB];
+    if (cc == c) continue;
+#pragma unroll
+    for (int x = 0; x < kGroups; ++x) M[x] = fmaxf(M[x], load_dev(part_ml_of(cc, x)));
+  }
+  auto weight = [&](float m, float mx) {  // an empty chunk (m = -inf) weighs 0
+    return m == -INFINITY ? 0.f : fast_exp2(m - mx);
+  };
+#pragma unroll
+  for (int x = 0; x < kGroups; ++x) Ls[x] = 0.f;
+  f32x4 acc[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Chunks in order; each chunk's partial loads are issued one chunk ahead.
+  f32x4 cur[kU], nxt[kU];
+  auto load_chunk = [&](int cc, f32x4 (&dst)[kU]) {
     if (cc == c) {
 #pragma unroll
-      for (int x = 0; x < kGroups; ++x) {
-        mc[x] = m_run[x];
-        lc[x] = l_run[x];
-#pragma unroll
-        for (int j = 0; j < kCB; ++j) oc[x][j] = O[x][j];
-      }
+      for (int u = 0; u < kU; ++u)
+        dst[u] = own[((src * kGroups + unit_x(u)) * kCB + unit_j(u)) * kWave + lane];
     } else {
-      const float* po = part_o_of(cc);
+      const float* po = part_o_of(cc, src);
 #pragma unroll
-      for (int x = 0; x < kGroups; ++x) {
-        const float* pml = part_ml_of(cc, x);
-        mc[x] = pml[0];
-        lc[x] = pml[1];
-#pragma unroll
-        for (int j = 0; j < kCB; ++j) oc[x][j] = *(const f32x4*)(po + ((x * kCB + j) * kWave + lane) * 4);
-      }
+      for (int u = 0; u < kU; ++u)
+        dst[u] = load_dev16(po + ((unit_x(u) * kCB + unit_j(u)) * kWave + lane) * 4);
     }
+  };
+  load_chunk(0, cur);
+  for (int cc = 0; cc < a.chunks; ++cc) {
+    if (cc + 1 < a.chunks) load_chunk(cc + 1, nxt);
+    float wx[kGroups];
 #pragma unroll
     for (int x = 0; x < kGroups; ++x) {
-      if (mc[x] == -INFINITY) continue;  // empty chunk: its partial is zero
-      const float mn = fmaxf(M[x], mc[x]);
-      const float wold = M[x] == -INFINITY ? 0.f : fast_exp2(M[x] - mn);
-      const float wnew = fast_exp2(mc[x] - mn);
-      Ls[x] = Ls[x] * wold + lc[x] * wnew;
-#pragma unroll
-      for (int j = 0; j < kCB; ++j) acc[x][j] = acc[x][j] * wold + oc[x][j] * wnew;
-      M[x] = mn;
+      float mc, lc;
+      if (cc == c) {
+        mc = m_run[x];
+        lc = l_run[x];
+      } else {
+        const float* pml = part_ml_of(cc, x);
+        mc = load_dev(pml);
+        lc = load_dev(pml + 1);
+      }
+      wx[x] = weight(mc, M[x]);
+      Ls[x] += wx[x] == 0.f ? 0.f : lc * wx[x];
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float w = wx[unit_x(u)];
+      if (w != 0.f) acc[u] += cur[u] * w;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
   }
+  // Lane li of a unit holds head li of group x, latent columns
+  // 16 * (src * kCB + j) + 4 * g .. + 3.
 #pragma unroll
-  for (int x = 0; x < kGroups; ++x) {
-#pragma unroll
-    for (int j = 0; j < kCB; ++j) acc[x][j] += poison;
-    store_out(x, acc[x], Ls[x]);
+  for (int u = 0; u < kU; ++u) {
+    const int x = unit_x(u), j = unit_j(u);
+    const int hx = hb * a.heads_per_block + x * 16 + li;
+    if (hx >= a.H) continue;
+    const float inv = Ls[x] > 0.f ? a.v_scale / Ls[x] : 0.f;
+    const f32x4 o = acc[u] + poison;
+    uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
+    const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
+                      (__bf16)(o[3] * inv)};
+    *(bf16x4*)(orow + 16 * (src * kCB + j) + 4 * g) = v;
   }
 }
 
