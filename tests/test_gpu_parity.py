@@ -409,6 +409,42 @@ def test_deterministic(H):
     assert np.array_equal(a.out_bits, b.out_bits)
 
 
+@pytest.mark.parametrize("layout", [1, 2])
+def test_many_chunk_merges_repeated_on_one_workspace(H, layout):
+    """The split merge under load: 64-token chunks (up to 32 per row, so
+    most workgroups publish and one per row and head block merges), 30
+    launches on one workspace without re-initialising it. Every launch must
+    give the same bits (the counters reset themselves, the merge order is
+    fixed whichever chunk arrives last) and the first must match the
+    oracle."""
+    import sparse_attention_decode_row_amd as dsa
+    rng = np.random.default_rng(31 + layout)
+    wl = WL.random_case(rng, rows=6, heads=64, D=512, block_size=64, max_len=3000,
+                        width=2048)
+    _announce("many-chunk merges, repeated", layout=layout)
+    plan = H.plan_for(wl, chunk_tokens=64, layout=layout)
+    info = plan.info()
+    print("plan", info)
+    assert info["chunks_per_row"] >= 16
+    q, pool = H.q_tensor(wl.q_bits), H.u8(wl.pool)
+    bt, sl, sel = H.i32(wl.block_tables), H.i32(wl.seq_lens), H.i32(wl.sel)
+    ws = plan.new_workspace()
+    outs = []
+    for _ in range(30):
+        out = torch.full_like(q, float("nan"))
+        plan.launch(q, pool, pool, bt, sl, sel, wl.k_scale, wl.v_scale, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    bits = [o.view(torch.int16).cpu().numpy() for o in outs]
+    for i, b in enumerate(bits[1:], 1):
+        assert np.array_equal(b, bits[0]), f"launch {i} differs from launch 0"
+    want = H.oracle_rows(wl, range(wl.rows))
+    err = H.normwise_err(outs[0].float().cpu().numpy().astype(np.float64), want)
+    print(f"many-chunk merges: max err {err.max():.3e}")
+    assert err.max() <= H.TOL
+    plan.close()
+
+
 # ------------------------------------------------------------ launch errors
 
 def test_launch_rejects_bad_arguments(H):
