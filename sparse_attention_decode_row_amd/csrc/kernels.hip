@@ -374,15 +374,17 @@ void dsa_decode_kernel(DecodeArgs a) {
   const int cstart = c * a.chunk_tokens + (c > 0 ? a.chunk_lead : 0);
   const int cend = (c + 1) * a.chunk_tokens + a.chunk_lead;
   const int32_t* srow = a.sel + (size_t)r * a.width;
-  // The length and up to 4 ids per thread are loaded first, from addresses
-  // clamped into their buffers (no branches), then the row's block-table
-  // entries go straight into LDS, then this wave's share of the query.
+  // The length and the first 2048 ids of the row (kPre per thread) are
+  // loaded first, from addresses clamped into their buffers (no branches),
+  // then the row's block-table entries go straight into LDS, then this
+  // wave's share of the query.
+  constexpr int kPre = (2048 + kThreads - 1) / kThreads;
   int L = a.seq_lens[r];
-  int tpre[4];  // ids tid + u*kThreads (u < 4); the rest of a wider row is loaded per window
+  int tpre[kPre];  // ids tid + u*kThreads (u < kPre); the rest of a wider row is loaded per window
 #pragma unroll
-  for (int u = 0; u < 4; ++u) tpre[u] = srow[min(tid + u * kThreads, a.width - 1)];
+  for (int u = 0; u < kPre; ++u) tpre[u] = srow[min(tid + u * kThreads, a.width - 1)];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < kPre; ++u)
     if (tid + u * kThreads >= a.width) tpre[u] = -1;
   const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
   const int nbt = min(a.bt_entries, kBtCap);
@@ -438,10 +440,10 @@ void dsa_decode_kernel(DecodeArgs a) {
     __syncthreads();
     // a hole (any negative id) or an id outside [0, L) sets nothing
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kPre; ++u)
       if (tpre[u] >= base && tpre[u] - base < span)
         atomicOr(&bitmap[(tpre[u] - base) >> 5], 1u << ((tpre[u] - base) & 31));
-    for (int j = tid + 4 * kThreads; j < a.width; j += kThreads) {
+    for (int j = tid + kPre * kThreads; j < a.width; j += kThreads) {
       const int t = srow[j];
       if (t >= base && t - base < span)
         atomicOr(&bitmap[(t - base) >> 5], 1u << ((t - base) & 31));
@@ -499,8 +501,8 @@ void dsa_decode_kernel(DecodeArgs a) {
       }
     };
 #pragma unroll
-    for (int u = 0; u < 4; ++u) place(tpre[u]);
-    for (int j = tid + 4 * kThreads; j < a.width; j += kThreads) place(srow[j]);
+    for (int u = 0; u < kPre; ++u) place(tpre[u]);
+    for (int j = tid + kPre * kThreads; j < a.width; j += kThreads) place(srow[j]);
     total += all;
     __syncthreads();  // the id table is complete; the bitmap is reused by the next window
   }
