@@ -61,8 +61,9 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this decode path is built and measured on one GPU; "
-                          "runs on more than one GPU are not part of it (see DESIGN.md "
-                          "for how it would shard)", "n_gpus": args.gpus}))
+                          "runs on more than one GPU are not part of it: rows shard "
+                          "across GPUs with no exchange, heads shard with one "
+                          "all-reduce after o_absorb", "n_gpus": args.gpus}))
         sys.exit(2)
 
     if args.workload == "latent_write":
