@@ -1058,78 +1058,80 @@ void dsa_decode_kernel(DecodeArgs a) {
   const int src = wave % kPVWaves, half = wave / kPVWaves;
   auto unit_x = [&](int u) { return (half * kU + u) / kCB; };
   auto unit_j = [&](int u) { return (half * kU + u) % kCB; };
-  // Per group: the largest reference over the chunks, each chunk's weight
-  // 2^(m_c - M) and the total sum, in fixed chunk order (deterministic
-  // whichever chunk merges).
-  float M[kGroups], Ls[kGroups];
-#pragma unroll
-  for (int x = 0; x < kGroups; ++x) M[x] = m_run[x];
-  for (int cc = 0; cc < a.chunks; ++cc) {
-    if (cc == c) continue;
-#pragma unroll
-    for (int x = 0; x < kGroups; ++x) M[x] = fmaxf(M[x], load_dev(part_ml_of(cc, x)));
-  }
-  auto weight = [&](float m, float mx) {  // an empty chunk (m = -inf) weighs 0
-    return m == -INFINITY ? 0.f : fast_exp2(m - mx);
-  };
-#pragma unroll
-  for (int x = 0; x < kGroups; ++x) Ls[x] = 0.f;
+  // Online log-sum-exp merge over batches of kB chunks in fixed order
+  // (deterministic whichever chunk merges): every load of a batch (each
+  // chunk's reference, sum and partial) is issued before any is used, so a
+  // batch costs one memory latency; a new batch maximum rescales what has
+  // been accumulated. A wave's units all belong to one head group, xw.
+  static_assert(kGroups == 1 || kU == kCB, "one head group per merging wave");
+  const int xw = unit_x(0);
+  constexpr int kB = 4;
+  float Mw = -INFINITY, Lw = 0.f;
   f32x4 acc[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Chunks in order; each chunk's partial loads are issued one chunk ahead.
-  f32x4 cur[kU], nxt[kU];
-  auto load_chunk = [&](int cc, f32x4 (&dst)[kU]) {
-    if (cc == c) {
+  const float m_own = kGroups == 1 ? m_run[0] : (xw == 0 ? m_run[0] : m_run[kGroups - 1]);
+  const float l_own = kGroups == 1 ? l_run[0] : (xw == 0 ? l_run[0] : l_run[kGroups - 1]);
+  for (int c0 = 0; c0 < a.chunks; c0 += kB) {
+    f32x4 pv[kB][kU];
+    float mv[kB], lv[kB];
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        dst[u] = own[((src * kGroups + unit_x(u)) * kCB + unit_j(u)) * kWave + lane];
-    } else {
-      const float* po = part_o_of(cc, src);
+    for (int b = 0; b < kB; ++b) {
+      const int cc = c0 + b;
+      if (cc >= a.chunks) {
+        mv[b] = -INFINITY;
+        lv[b] = 0.f;
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
-        dst[u] = load_dev16(po + ((unit_x(u) * kCB + unit_j(u)) * kWave + lane) * 4);
-    }
-  };
-  load_chunk(0, cur);
-  for (int cc = 0; cc < a.chunks; ++cc) {
-    if (cc + 1 < a.chunks) load_chunk(cc + 1, nxt);
-    float wx[kGroups];
+        for (int u = 0; u < kU; ++u) pv[b][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if (cc == c) {
+        mv[b] = m_own;
+        lv[b] = l_own;
 #pragma unroll
-    for (int x = 0; x < kGroups; ++x) {
-      float mc, lc;
-      if (cc == c) {
-        mc = m_run[x];
-        lc = l_run[x];
+        for (int u = 0; u < kU; ++u)
+          pv[b][u] = own[((src * kGroups + xw) * kCB + unit_j(u)) * kWave + lane];
       } else {
-        const float* pml = part_ml_of(cc, x);
-        mc = load_dev(pml);
-        lc = load_dev(pml + 1);
+        const float* pml = part_ml_of(cc, xw);
+        mv[b] = load_dev(pml);
+        lv[b] = load_dev(pml + 1);
+        const float* po = part_o_of(cc, src);
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          pv[b][u] = load_dev16(po + ((xw * kCB + unit_j(u)) * kWave + lane) * 4);
       }
-      wx[x] = weight(mc, M[x]);
-      Ls[x] += wx[x] == 0.f ? 0.f : lc * wx[x];
     }
+    // the batch's maximum; what is accumulated so far is rescaled to it (an
+    // empty chunk has m = -inf and weighs 0)
+    float mb = Mw;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) mb = fmaxf(mb, mv[b]);
+    const float sc = Mw == -INFINITY ? 0.f : fast_exp2(Mw - mb);
+    Lw *= sc;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc[u] *= sc;
+    Mw = mb;
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const float w = mv[b] == -INFINITY ? 0.f : fast_exp2(mv[b] - mb);
+      if (w != 0.f) {
+        Lw += lv[b] * w;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc[u] += pv[b][u] * w;
+      }
+    }
+  }
+  // Lane li of a unit holds head li of group xw, latent columns
+  // 16 * (src * kCB + j) + 4 * g .. + 3.
+  const int hx = hb * a.heads_per_block + xw * 16 + li;
+  if (hx < a.H) {
+    const float inv = Lw > 0.f ? a.v_scale / Lw : 0.f;
+    uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float w = wx[unit_x(u)];
-      if (w != 0.f) acc[u] += cur[u] * w;
+      const f32x4 o = acc[u] + poison;
+      const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
+                        (__bf16)(o[3] * inv)};
+      *(bf16x4*)(orow + 16 * (src * kCB + unit_j(u)) + 4 * g) = v;
     }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) cur[u] = nxt[u];
-  }
-  // Lane li of a unit holds head li of group x, latent columns
-  // 16 * (src * kCB + j) + 4 * g .. + 3.
-#pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int x = unit_x(u), j = unit_j(u);
-    const int hx = hb * a.heads_per_block + x * 16 + li;
-    if (hx >= a.H) continue;
-    const float inv = Ls[x] > 0.f ? a.v_scale / Ls[x] : 0.f;
-    const f32x4 o = acc[u] + poison;
-    uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
-    const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
-                      (__bf16)(o[3] * inv)};
-    *(bf16x4*)(orow + 16 * (src * kCB + j) + 4 * g) = v;
   }
 }
 
