@@ -192,7 +192,19 @@ void plan_layout(dsa_decode_plan_s* plan) {
   plan->chunk_lead = 0;
   if (plan->chunks > 1 && p.chunk_tokens == 0) {
     const int64_t lead = std::min<int64_t>(2 * kTileTokens, kMaxChunkTokens - ct);
-    if (lead > 0 && ct > lead) plan->chunk_lead = (int)lead;
+    if (lead > 0 && ct > lead) {
+      plan->chunk_lead = (int)lead;
+      // The lead can leave the last chunk without any rank: count the chunks
+      // again. If chunk 0 then holds every rank, one chunk of that size it is.
+      const int64_t c2 = std::max<int64_t>(1, (wmax - lead + ct - 1) / ct);
+      if (c2 == 1) {
+        plan->chunks = 1;
+        plan->chunk_lead = 0;
+        plan->chunk_tokens = (int)((wmax + kTileTokens - 1) / kTileTokens * kTileTokens);
+      } else {
+        plan->chunks = (int)c2;
+      }
+    }
   }
 
   WorkspaceLayout& L = plan->ws;

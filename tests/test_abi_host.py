@@ -314,3 +314,53 @@ def test_masked_reference_without_gpu_is_a_device_error(native):
     with pytest.raises(native.DsaDecodeError) as e:
         _reference_call(native)
     assert e.value.status == native.DSA_DECODE_ERR_DEVICE
+
+
+def test_planner_invariants_over_random_geometries(native):
+    """Property test of the planner (host-only plans): for any valid
+    geometry the chunks cover every rank a row can have, no workgroup's
+    row table exceeds its 2048 LDS entries, the grid covers every (row,
+    chunk, head block) unit in whole rounds of 8 (whole blocks of 8
+    sequences when rows are co-scheduled), and the workspace holds the
+    exported selection plus, when rows are split, every partial."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=300, deadline=None)
+    @given(rows=st.integers(1, 300), heads=st.integers(1, 200),
+           D=st.sampled_from([64, 128, 256, 512]), B=st.sampled_from([4, 16, 64]),
+           width=st.integers(1, 5000), L=st.integers(1, 300000),
+           ct=st.integers(0, 32), layout=st.integers(0, 2), k=st.integers(0, 6))
+    def check(rows, heads, D, B, width, L, ct, layout, k):
+        if k > 1 and rows % k:
+            k = 1
+        stride = -(-L // B)
+        p = native.Plan(device=-1, num_rows=rows, num_q_heads=heads, kv_lora_rank=D,
+                        block_size=B, index_kpool=4 if B % 4 == 0 else 1, sel_width=width,
+                        block_table_stride=stride, max_seq_len=L, sm_scale=0.1,
+                        chunk_tokens=64 * ct, layout=layout, rows_per_sequence=k)
+        info = p.info()
+        wmax = min(width, L)
+        C, T, lead, HB = (info["chunks_per_row"], info["chunk_tokens"], info["chunk_lead"],
+                          info["head_blocks"])
+        assert T % 64 == 0 and 64 <= T <= 2048
+        assert C * T + lead >= wmax                  # every rank is in some chunk
+        assert T + lead <= 2048                      # chunk 0's row table fits
+        assert (C - 1) * T + lead < max(wmax, 1) or C == 1   # no chunk is always empty
+        assert HB == -(-heads // info["heads_per_block"])
+        assert info["heads_per_block"] == (16 if info["layout"] == 2 else 32)
+        assert info["merges_chunks"] == (C > 1)
+        units = rows * C
+        if info["rows_per_sequence"] > 1:
+            G = info["rows_per_sequence"] * C
+            assert info["workgroups"] == -(-(rows // info["rows_per_sequence"]) // 8) * 8 * G * HB
+        else:
+            assert info["workgroups"] == -(-units // 8) * 8 * HB
+        assert info["workgroups"] >= units * HB
+        need = rows * width * 12 + rows * 4 + 2 * rows * HB * 4
+        if C > 1:
+            slots = rows * HB * C * info["heads_per_block"]
+            need += slots * D * 4 + slots * 2 * 4
+        assert need <= p.workspace_bytes <= need + 8 * 256
+        p.close()
+
+    check()
