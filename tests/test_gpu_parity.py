@@ -111,14 +111,14 @@ def test_verify_rows_co_scheduled_per_sequence(H):
     assert err.max() <= H.TOL
 
 
-@pytest.mark.parametrize("k,chunk_tokens", [(3, 64), (5, 0)])
-def test_co_scheduled_rows_with_padding_and_splits(H, k, chunk_tokens):
+@pytest.mark.parametrize("k,chunk_tokens,heads", [(3, 64, 40), (5, 0, 40), (2, 64, 16), (4, 0, 12)])
+def test_co_scheduled_rows_with_padding_and_splits(H, k, chunk_tokens, heads):
     """A sequence count that leaves a block of 8 partly empty, with and
-    without split chunks: same bits as independent scheduling, oracle parity
-    on every row."""
+    without split chunks, in 32-head and 16-head blocks: same bits as
+    independent scheduling, oracle parity on every row."""
     rng = np.random.default_rng(77 + k)
     seqs = 5
-    wl = WL.random_case(rng, rows=seqs * k, heads=40, D=128, block_size=16,
+    wl = WL.random_case(rng, rows=seqs * k, heads=heads, D=128, block_size=16,
                         width=300, max_len=900)
     _announce("co-scheduled", rows=wl.rows, k=k, chunk_tokens=chunk_tokens)
     base = H.run_gpu(wl, chunk_tokens=chunk_tokens)
