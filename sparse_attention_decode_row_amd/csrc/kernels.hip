@@ -350,9 +350,11 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Workgroup -> (row, chunk, head block). The head blocks of one (row,
   // chunk) read the same latent rows, so they get ids 8 apart: the same XCD
   // (ids are dealt to the 8 XCDs round-robin) and its L2 serves the second
-  // read. Ids come in rounds of 8 (one per XCD) per head block. When the
-  // rows of a sequence are co-scheduled, its group_units (row, chunk) units
-  // take group_units consecutive rounds on one XCD, for the same reason.
+  // read. Ids come in rounds of 8 (one per XCD) per head block. When a row
+  // is split into chunks, or the rows of a sequence are co-scheduled, the
+  // group_units (row, chunk) units of the sequence take group_units
+  // consecutive rounds on one XCD, for the same reason (they share the
+  // query and ids, or most of the latent rows).
   const int bid = blockIdx.x;
   const int hb = (bid >> 3) % a.head_blocks;
   int rc = (bid / (8 * a.head_blocks)) * 8 + (bid & 7);

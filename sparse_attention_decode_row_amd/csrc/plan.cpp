@@ -229,12 +229,15 @@ void plan_layout(dsa_decode_plan_s* plan) {
   L.total = off;
   // Workgroup ids: the head blocks of one (row, chunk) are 8 apart, so the
   // (row, chunk) count is padded to a multiple of 8 (padding ids exit).
-  // Co-scheduled sequences: the rows_per_sequence x chunks units of one
-  // sequence take consecutive rounds of 8 ids on one XCD, 8 sequences per
-  // block of rounds, so the unit count is padded to whole blocks.
+  // Grouped units: the rows_per_sequence x chunks units of one sequence (a
+  // sequence is one row unless rows are co-scheduled) take consecutive
+  // rounds of 8 ids on one XCD, 8 sequences per block of rounds, so the unit
+  // count is padded to whole blocks. The units of a group read the same
+  // query rows and ids (the chunks of a row) or largely the same latent rows
+  // (the rows of a sequence), which that XCD's L2 then serves once.
   const int64_t k = p.rows_per_sequence > 1 ? p.rows_per_sequence : 1;
-  plan->group_units = k > 1 ? (int)(k * plan->chunks) : 1;
-  if (k > 1) {
+  plan->group_units = (k > 1 || plan->chunks > 1) ? (int)(k * plan->chunks) : 1;
+  if (plan->group_units > 1) {
     const int64_t seqs = R / k;
     plan->workgroups = (int)((seqs + 7) / 8 * 8 * plan->group_units * plan->head_blocks);
   } else {

@@ -123,8 +123,9 @@ def test_split_plan(native, kw, chunks, ct):
     assert info["chunk_tokens"] == ct
     assert info["merges_chunks"] == (chunks > 1)
     rows = kw.get("num_rows", 128)
-    # (row, chunk) pairs padded to a multiple of 8, times the head blocks
-    assert info["workgroups"] == (rows * chunks + 7) // 8 * 8 * info["head_blocks"]
+    # one row's chunks are grouped on one XCD: rows padded to a multiple of
+    # 8, times the chunks and the head blocks (unsplit rows: the same)
+    assert info["workgroups"] == (rows + 7) // 8 * 8 * chunks * info["head_blocks"]
     heads = kw.get("num_q_heads", 64)
     small = kw.get("layout", 0) == 2 or heads <= 16
     assert info["layout"] == (2 if small else 1)
@@ -252,10 +253,12 @@ def test_rows_per_sequence_grid(native):
 
 
 def test_rows_per_sequence_mapping_is_a_bijection():
-    """The kernel's workgroup -> (row, chunk) map for co-scheduled rows,
-    restated here: every unit is hit exactly once, the units of a sequence
-    share an XCD (id mod 8) and head blocks of one unit are 8 ids apart."""
-    for seqs, k, chunks, hb in [(64, 4, 1, 2), (5, 3, 2, 1), (9, 2, 3, 4), (1, 5, 1, 1)]:
+    """The kernel's workgroup -> (row, chunk) map for grouped units (the
+    rows of a co-scheduled sequence, or the chunks of a split row), restated
+    here: every unit is hit exactly once, the units of a sequence share an
+    XCD (id mod 8) and head blocks of one unit are 8 ids apart."""
+    for seqs, k, chunks, hb in [(64, 4, 1, 2), (5, 3, 2, 1), (9, 2, 3, 4), (1, 5, 1, 1),
+                                (32, 1, 4, 2), (13, 1, 3, 2), (3, 1, 11, 4)]:
         G = k * chunks
         blocks = -(-seqs // 8)
         grid = blocks * 8 * G * hb
@@ -350,8 +353,10 @@ def test_planner_invariants_over_random_geometries(native):
         assert info["heads_per_block"] == (16 if info["layout"] == 2 else 32)
         assert info["merges_chunks"] == (C > 1)
         units = rows * C
-        if info["rows_per_sequence"] > 1:
-            G = info["rows_per_sequence"] * C
+        # the rows_per_sequence x chunks units of a sequence (one row when
+        # rows are not co-scheduled) are grouped whenever there is more than one
+        G = info["rows_per_sequence"] * C
+        if G > 1:
             assert info["workgroups"] == -(-(rows // info["rows_per_sequence"]) // 8) * 8 * G * HB
         else:
             assert info["workgroups"] == -(-units // 8) * 8 * HB
