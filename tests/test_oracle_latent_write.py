@@ -13,6 +13,10 @@ What pins what:
   * RMSNorm: closed forms (a constant row normalises to its sign; a one-hot
     row to sqrt(D) at the hot position; a zero row with eps > 0 to zero), and
     invariance of the codes to scaling the row by a power of two (eps = 0).
+  * Where eps sits: rows whose mean square is comparable to eps, with closed
+    forms (eps = c^2 on a constant row c gives 1/sqrt(2); eps = 3 * mean
+    square gives exactly half of each entry over the rms). eps added after
+    the root, or scaled by D, fails both.
   * Addressing: a pool pre-filled with a sentinel, rows written to hand-placed
     slots, every other byte untouched; negative slots write nothing.
 """
@@ -142,3 +146,31 @@ def test_writer_rejects_bad_arguments(oracle_mod):
         _write(oracle_mod, np.ones((1, D)), np.ones(D), [8 * 16], D=D)  # past the pool
     with pytest.raises(ValueError):
         _write(oracle_mod, np.ones((1, D)), np.ones(D), [0], D=D, eps=-1.0)
+
+
+def test_eps_sits_inside_the_root_constant_row(oracle_mod):
+    # A constant row c with eps = c^2: the mean square is c^2, so the row
+    # normalises to c / sqrt(2 c^2) = 1/sqrt(2) (times weight and 1/kv_scale).
+    # eps added after the root (c / (|c| + eps)) gives ~1, a scaled eps
+    # (D * eps, eps / D) gives 1/sqrt(D + 1) or ~1: all fail.
+    D = 64
+    c = 2.0 ** -10
+    w = np.linspace(0.5, 2.0, D)
+    pool, vals = _write(oracle_mod, np.full((1, D), c), w, [0], D=D, eps=c * c, inv=4.0)
+    wb = oracle_mod.bf16(bf16_bits(w))
+    np.testing.assert_allclose(vals[0], wb * 4.0 / math.sqrt(2.0), rtol=1e-15)
+    np.testing.assert_array_equal(pool[:D], oracle_mod.fp8_e4m3fn_encode(vals[0]))
+
+
+def test_eps_three_times_the_mean_square_halves_the_row(oracle_mod):
+    # Entries +-2^-8 (mean square 2^-16) with eps = 3 * 2^-16: the root is
+    # sqrt(4 * 2^-16) = 2^-7, so every entry maps to +-1/2 exactly.
+    D = 128
+    sign = np.where(np.arange(D) % 3 == 0, -1.0, 1.0)
+    row = sign * 2.0 ** -8
+    pool, vals = _write(oracle_mod, row[None], np.ones(D), [1], D=D,
+                        eps=3.0 * 2.0 ** -16, inv=1.0)
+    np.testing.assert_array_equal(vals[0], sign * 0.5)
+    # 0.5 is an FP8 code: 0x30 (e = 6, m = 0), with the sign bit for -0.5
+    want = np.where(sign < 0, 0xB0, 0x30).astype(np.uint8)
+    np.testing.assert_array_equal(pool[D:2 * D], want)
