@@ -45,8 +45,9 @@ def parse():
                     help="latent_write: rows written per launch")
     ap.add_argument("--sets", type=int, default=4,
                     help="distinct input batches cycled through")
-    ap.add_argument("--cpu-rows", type=int, default=128,
-                    help="rows of the workload the CPU oracle is timed on (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="rows of the workload the CPU oracle is timed on, on all its "
+                         "threads (1/32 of them on one thread; 0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference dispatch for HBM counter calibration)")
@@ -251,8 +252,12 @@ def measured_traffic(workload, kernel="dsa_decode_kernel", source="kernels.hip",
 
 
 def cpu_baseline(wl, pool_dev, batch, nrows):
-    """The CPU oracle, as it stands, on the first `nrows` rows of the first
-    batch (all heads, the full selection of each row), on this host's cores."""
+    """The CPU oracle, as it stands, on the first rows of the first batch
+    (all heads, the full selection of each row): one warm-up run, then the
+    median of 3 timed runs on every thread the oracle uses (the first
+    `nrows` rows), and the same on one thread (a smaller sample of rows)."""
+    import statistics
+
     import numpy as np
     import torch
 
@@ -260,6 +265,7 @@ def cpu_baseline(wl, pool_dev, batch, nrows):
     import workloads as WL
 
     rows = list(range(min(nrows, wl.rows)))
+    rows_1t = rows[:max(1, len(rows) // 32)]
     assert wl.cache_stride_bytes == wl.block_size * wl.D
     # Pages the sample touches, renumbered compactly into a host pool that is
     # zero (untouched, never faulted in) except for the selected latent rows,
@@ -282,21 +288,38 @@ def cpu_baseline(wl, pool_dev, batch, nrows):
     sub = np.zeros((pages.size * wl.block_size, wl.D), dtype=np.uint8)
     sub[dst_rows] = got
     sub = sub.ravel()
-    q = batch[0].view(torch.int16).cpu().numpy().view(np.uint16)[rows]
-    sel = wl.sel[rows]
+    q_all = batch[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    sel_all, sl_all = wl.sel, wl.seq_lens
+
+    def tokens_of(rs):
+        return sum(int(np.unique(sel_all[r][(sel_all[r] >= 0) & (sel_all[r] < sl_all[r])]).size)
+                   for r in rs)
+
+    def run(rs, threads):
+        k = len(rs)
+        t = time.perf_counter()
+        oracle.decode(q_all[rs], sub, None, bt[:k], sl_all[rs], sel_all[rs],
+                      block_size=wl.block_size, bt_stride=wl.bt_stride,
+                      cache_stride_bytes=wl.cache_stride_bytes, sm_scale=wl.sm_scale,
+                      k_scale=wl.k_scale, v_scale=wl.v_scale, num_threads=threads)
+        return time.perf_counter() - t
+
     threads = oracle.max_threads()
-    t = time.perf_counter()
-    oracle.decode(q, sub, None, bt, wl.seq_lens[rows], sel, block_size=wl.block_size,
-                  bt_stride=wl.bt_stride, cache_stride_bytes=wl.cache_stride_bytes,
-                  sm_scale=wl.sm_scale, k_scale=wl.k_scale, v_scale=wl.v_scale,
-                  num_threads=threads)
-    dt = time.perf_counter() - t
-    tokens = sum(int(np.unique(sel[i][(sel[i] >= 0) & (sel[i] < wl.seq_lens[r])]).size)
-                 for i, r in enumerate(rows))
+    run(rows[:max(1, len(rows) // 8)], threads)                  # warm-up
+    times = [run(rows, threads) for _ in range(3)]
+    times_1t = [run(rows_1t, 1) for _ in range(3)]
+    dt, dt1 = statistics.median(times), statistics.median(times_1t)
+    tokens, tokens_1t = tokens_of(rows), tokens_of(rows_1t)
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {wl.rows} rows of the same workload (all "
                       f"{wl.heads} heads, {tokens} selected tokens), float64 C oracle, "
-                      f"{dt:.2f} s wall"}
+                      f"median of 3 runs after one warm-up: "
+                      f"{', '.join(f'{x:.2f}' for x in times)} s",
+            "one_thread": {"value": tokens_1t / dt1, "unit": "tokens/s",
+                           "sample": f"{len(rows_1t)} rows ({tokens_1t} selected tokens), "
+                                     f"median of 3: {', '.join(f'{x:.2f}' for x in times_1t)} s"},
+            "nproc": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def bench_latent_write(args):

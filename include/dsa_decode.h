@@ -104,12 +104,31 @@ typedef struct dsa_decode_params {
    * and served to the others by that XCD's L2. num_rows must be a multiple
    * of k. The result does not depend on it. */
   int32_t rows_per_sequence;
+  /* Bit set of DSA_DECODE_FLAG_* (0: none). */
+  int32_t flags;
+  /* Width of a rope tail carried by every cached token after its latent.
+   * 0: NoPE, the latent is the whole token ([attend] module doc, "NoPE, and
+   * why no common/ kernel would do"). 64: the DeepSeek-V4-style token that
+   * the same passage and decode_attention's scale comment describe: each
+   * token is kv_lora_rank (must be 512) latent bytes followed by 64 bytes of
+   * an already rotated rope tail, 576 FP8 E4M3FN bytes in all; q carries
+   * 576 values per head, the scores run over all 576 (token t's own tail
+   * against q's tail, never the next token's bytes), the values and the
+   * output are the first 512. Nothing is rotated here. Any other value is
+   * DSA_DECODE_ERR_UNSUPPORTED. */
+  int32_t qk_rope_dim;
   int32_t reserved[2]; /* must be zero */
 } dsa_decode_params;
 
 #define DSA_DECODE_LAYOUT_AUTO 0
 #define DSA_DECODE_LAYOUT_HEADS32 1
 #define DSA_DECODE_LAYOUT_HEADS16 2
+
+/* flags: every launch also writes the normalised selection (ids, counts and
+ * byte offsets) into the workspace, for dsa_decode_read_selection. Off by
+ * default: the decode itself never needs it, and it costs 12 bytes of
+ * workspace and of HBM writes per selection slot. */
+#define DSA_DECODE_FLAG_EXPORT_SELECTION 1
 
 /* Opaque plan: validated geometry plus the launch decomposition. Host
  * memory owned by the library; free it with dsa_decode_plan_destroy. */
@@ -134,6 +153,16 @@ typedef struct dsa_decode_plan_info {
   int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32 or _HEADS16 (resolved) */
   int32_t heads_per_block; /* 32 or 16 */
   int32_t rows_per_sequence; /* rows co-scheduled on one XCD (1: none) */
+  int32_t flags;           /* params.flags */
+  int32_t qk_rope_dim;     /* params.qk_rope_dim */
+  /* Byte offsets inside the workspace, for diagnostics and tests:
+   *   status_offset    int32, 0 while healthy; set to 1 by a launch whose
+   *                    split merge gave up waiting (see dsa_decode_launch)
+   *   counters_offset  int32 [2][num_rows * head_blocks]: chunks arrived,
+   *                    then partials published, per (row, head block);
+   *                    zero between launches */
+  uint64_t status_offset;
+  uint64_t counters_offset;
 } dsa_decode_plan_info;
 
 /* Validate params and build a plan.
@@ -151,9 +180,10 @@ int dsa_decode_plan(const dsa_decode_params* params, int device,
 /* Free a plan (NULL is ignored). */
 void dsa_decode_plan_destroy(dsa_decode_plan_t plan);
 
-/* Device scratch bytes dsa_decode_launch needs (selection ids, token byte
- * offsets, per-row counts, per-row arrival counters, and split partials when
- * chunks_per_row > 1). The caller allocates it; 0 for a NULL plan. */
+/* Device scratch bytes dsa_decode_launch needs (a status word, per-row
+ * arrival counters, split partials when chunks_per_row > 1, and with
+ * DSA_DECODE_FLAG_EXPORT_SELECTION the selection ids, token byte offsets and
+ * per-row counts). The caller allocates it; 0 for a NULL plan. */
 size_t dsa_decode_workspace_bytes(dsa_decode_plan_t plan);
 
 /* Zero a workspace for `plan` on `stream` (a fill kernel, no memset, so it
@@ -187,6 +217,14 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
  *                zeroed once by dsa_decode_workspace_init for this plan;
  *                overwritten; must not be shared by launches in flight.
  * k_scale, v_scale: per-tensor dequantisation scales (finite).
+ * Split rows (chunks_per_row > 1): the last chunk of a (row, head block) to
+ * finish waits for the others' partials, which every other chunk publishes
+ * after it has arrived, so the wait ends within microseconds. Should it not
+ * end within about 0.1 s (a broken counter), that (row, head block) is
+ * written as NaN and the workspace's status word is set: from then on every
+ * output of every launch on this workspace is NaN, until
+ * dsa_decode_workspace_init zeroes it again. The counters themselves return
+ * to zero once the late chunks publish.
  * Device-side preconditions (not checked by the kernels): every page id a
  * selected token maps to lies inside the pool; the pool holds fewer than
  * 2^32 latent rows (page * cache_stride_bytes / kv_lora_rank + block_size
@@ -202,7 +240,9 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q,
                       void* stream);
 
 /* Copy the normalised selection the last launch on `workspace` computed
- * (what the attention consumed) into caller device memory, on `stream`:
+ * (what the attention consumed) into caller device memory, on `stream`.
+ * Only for plans made with DSA_DECODE_FLAG_EXPORT_SELECTION (otherwise
+ * DSA_DECODE_ERR_INVALID):
  *   ids      int32  [num_rows, sel_width]: row r's distinct valid ids in
  *            ascending order in its first counts[r] entries; the rest is
  *            unspecified
@@ -283,7 +323,7 @@ const char* dsa_decode_last_error(void);
 /* ABI version of this header (major * 100 + minor). */
 int dsa_decode_version(void);
 
-#define DSA_DECODE_VERSION 302
+#define DSA_DECODE_VERSION 400
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,8 @@ DSA_DECODE_ERR_DEVICE = -3
 DSA_DECODE_ERR_WORKSPACE = -4
 DSA_DECODE_ERR_LAUNCH = -5
 
+DSA_DECODE_FLAG_EXPORT_SELECTION = 1
+
 EXPORTED_SYMBOLS = (
     "dsa_decode_plan", "dsa_decode_plan_destroy", "dsa_decode_workspace_bytes",
     "dsa_decode_workspace_init", "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
@@ -62,6 +64,8 @@ class Params(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("layout", ctypes.c_int32),
         ("rows_per_sequence", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("qk_rope_dim", ctypes.c_int32),
         ("reserved", ctypes.c_int32 * 2),
     ]
 
@@ -80,6 +84,10 @@ class PlanInfo(ctypes.Structure):
         ("layout", ctypes.c_int32),
         ("heads_per_block", ctypes.c_int32),
         ("rows_per_sequence", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+        ("qk_rope_dim", ctypes.c_int32),
+        ("status_offset", ctypes.c_uint64),
+        ("counters_offset", ctypes.c_uint64),
     ]
 
     def as_dict(self) -> dict:
@@ -163,22 +171,27 @@ def _stream(stream) -> Optional[int]:
 
 class Plan:
     """A validated decode geometry (dsa_decode_plan). device=-1 builds a
-    host-only plan (validation and sizing, no launches)."""
+    host-only plan (validation and sizing, no launches). export_selection
+    sets DSA_DECODE_FLAG_EXPORT_SELECTION (needed by read_selection)."""
 
     def __init__(self, *, num_rows: int, num_q_heads: int, kv_lora_rank: int,
                  block_size: int, index_kpool: int, sel_width: int,
                  block_table_stride: int, max_seq_len: int, sm_scale: float,
                  num_kv_heads: int = 1, cache_stride_bytes: int = 0,
                  chunk_tokens: int = 0, layout: int = 0, rows_per_sequence: int = 0,
+                 export_selection: bool = False, flags: int = 0, qk_rope_dim: int = 0,
                  device: Optional[int] = None):
         if device is None:
             import torch
             device = torch.cuda.current_device()
         self._lib = lib()
+        if export_selection:
+            flags |= DSA_DECODE_FLAG_EXPORT_SELECTION
         self.params = Params(num_rows, num_q_heads, num_kv_heads, kv_lora_rank,
                              block_size, index_kpool, sel_width, block_table_stride,
                              cache_stride_bytes, max_seq_len, sm_scale, chunk_tokens,
-                             layout, rows_per_sequence, (ctypes.c_int32 * 2)(0, 0))
+                             layout, rows_per_sequence, flags, qk_rope_dim,
+                             (ctypes.c_int32 * 2)(0, 0))
         h = ctypes.c_void_p()
         _check(self._lib.dsa_decode_plan(ctypes.byref(self.params), int(device),
                                          ctypes.byref(h)))
@@ -271,7 +284,10 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
            workspace=None, stream=None):
     """One-shot helper: plan, allocate out/workspace with torch, launch.
     q: bf16 [R, H, D] on the GPU; returns out (bf16 [R, H, D]). A workspace
-    passed in must have been zeroed for this geometry (Plan.workspace_init)."""
+    passed in must have been zeroed for this geometry (Plan.workspace_init).
+    Buffers it allocates come from the launch stream's pool and are marked as
+    used by that stream, so torch does not hand them out again before the
+    launch has finished with them."""
     import torch
     R, H, D = q.shape
     plan = Plan(num_rows=R, num_q_heads=H, kv_lora_rank=D, block_size=block_size,
@@ -279,13 +295,21 @@ def decode(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *,
                 block_table_stride=block_table_stride, max_seq_len=max_seq_len,
                 sm_scale=sm_scale, cache_stride_bytes=cache_stride_bytes,
                 chunk_tokens=chunk_tokens, device=q.device.index)
+    if stream is None or isinstance(stream, int):
+        ts = torch.cuda.current_stream(q.device) if stream is None else \
+            torch.cuda.ExternalStream(stream, device=q.device)
+    else:
+        ts = stream
     try:
-        if out is None:
-            out = torch.empty_like(q)
-        if workspace is None:
-            workspace = plan.new_workspace(q.device.index, stream=stream)
+        with torch.cuda.stream(ts):
+            if out is None:
+                out = torch.empty_like(q)
+                out.record_stream(ts)
+            if workspace is None:
+                workspace = plan.new_workspace(q.device.index, stream=ts)
+                workspace.record_stream(ts)
         plan.launch(q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
-                    k_scale, v_scale, out, workspace, stream=stream)
+                    k_scale, v_scale, out, workspace, stream=ts)
     finally:
         plan.close()
     return out
@@ -314,7 +338,7 @@ def masked_reference(q, k_cache, v_cache, block_tables, seq_lens, sel_indices, *
     R, H, D = q.shape
     params = Params(R, H, 1, D, block_size, index_kpool, sel_indices.shape[1],
                     block_table_stride, cache_stride_bytes, max_seq_len, sm_scale, 0, 0, 0,
-                    (ctypes.c_int32 * 2)(0, 0))
+                    0, 0, (ctypes.c_int32 * 2)(0, 0))
     if out is None:
         out = torch.empty((R, H, D), dtype=torch.float32, device=q.device)
     _check(lib().dsa_decode_masked_reference(

@@ -254,9 +254,10 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const int32_t* sel;
   uint16_t* out;
-  int32_t* ws_ids;       // [R, W] distinct ids, ascending (exported)
-  uint64_t* ws_offsets;  // [R, W] their latent-row byte offsets (exported)
-  int32_t* ws_counts;    // [R]
+  int32_t* ws_status;    // 0 healthy; 1 once a split merge gave up waiting (outputs NaN until re-init)
+  int32_t* ws_ids;       // [R, W] distinct ids, ascending (export only)
+  uint64_t* ws_offsets;  // [R, W] their latent-row byte offsets (export only)
+  int32_t* ws_counts;    // [R] (export only)
   int32_t* ws_arrivals;  // [2][R * head_blocks] chunks arrived / partials published; reset by the merger
   float* part_o;         // [R, head_blocks, C, heads_per_block, D] (per-wave register order)
   float* part_ml;        // [R, head_blocks, C, heads_per_block, 2]
@@ -278,7 +279,13 @@ struct DecodeArgs {
   int group_units;   // (row, chunk) units co-scheduled on one XCD (1: none)
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
+  int export_sel;    // write the selection (ids, offsets, counts) for the read-back hook
 };
+
+// Longest a merging workgroup waits for the other chunks' partials, in ticks
+// of the 100 MHz real-time counter (0.1 s): they have all arrived when the
+// wait starts, so it ends within microseconds unless a counter is broken.
+constexpr uint64_t kMergeWaitTicks = 10000000;
 
 // Waves of a workgroup: per 16-head group two scoring waves, each taking
 // 32 tokens of a 64-token tile (QK^T and the softmax weights), and as many
@@ -329,7 +336,6 @@ void dsa_decode_kernel(DecodeArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
-  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kMaxChunkTokens];
   // softmax weights of a tile as PV B operands: [tile parity][group][operand half][lane] x 16 bytes
   __shared__ __attribute__((aligned(16))) i32x4 xch_p[2][kGroups][2][kWave];
   __shared__ int xch_e[2][kGroups][4][16];  // their E8M0 exponent bytes, per 16-token block and head
@@ -431,7 +437,13 @@ void dsa_decode_kernel(DecodeArgs a) {
   u32x4* wrank4 = (u32x4*)(smem + kSmemBytes / 4);
   const DSA_LDS uint32_t* wrank_l = (const DSA_LDS uint32_t*)(smem + kSmemBytes / 4);
   if (tid == 0) flag_sh = 0;
-  const bool exporter = hb == 0;  // exports the ids and offsets of the row (after the loop)
+  // A workspace whose status word is set makes every output NaN (read now,
+  // used at the stores).
+  const bool sticky_bad = __hip_atomic_load(a.ws_status, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) != 0;
+  // Head block 0 exports the row's ids and byte offsets, straight from the
+  // placement below, when the read-back hook is wanted.
+  const bool exporter = hb == 0 && a.export_sel;
   const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
   int total = 0;
   for (int base = 0; base < L; base += kWinWords * 32) {
@@ -497,8 +509,12 @@ void dsa_decode_kernel(DecodeArgs a) {
           const int pi = a.bs_shift >= 0 ? t >> a.bs_shift : t / a.block_size;
           const int slot = t - pi * a.block_size;
           const uint32_t page = (uint32_t)(pi < nbt ? btl[pi] : bt[pi]);
-          rows_lds[rank - cstart] = page * a.stride_rows + (uint32_t)slot;
-          if (exporter) ids_lds[rank - cstart] = t;
+          const uint32_t lrow = page * a.stride_rows + (uint32_t)slot;
+          rows_lds[rank - cstart] = lrow;
+          if (exporter) {
+            a.ws_ids[(size_t)r * a.width + rank] = t;
+            a.ws_offsets[(size_t)r * a.width + rank] = (uint64_t)lrow * (uint64_t)D;
+          }
         }
       }
     };
@@ -510,6 +526,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
   const int n = max(0, min(cend - cstart, total - cstart));
   const int ntiles = (n + kTile - 1) / kTile;
+  if (exporter && c == 0 && tid == 0) a.ws_counts[r] = total;
 
   // pad the row table to whole tiles with the last real row (loaded,
   // weighted by zero)
@@ -951,24 +968,13 @@ void dsa_decode_kernel(DecodeArgs a) {
     m_run[x] = xch_m[x][lane];
   }
 
-  // The ids of the row and their byte offsets (head block 0 exports them).
-  if (exporter && is_qk) {
-    int32_t* idw = a.ws_ids + (size_t)r * a.width + cstart;
-    uint64_t* offw = a.ws_offsets + (size_t)r * a.width + cstart;
-    for (int i = tid; i < n; i += kQKWaves * kWave) {
-      idw[i] = ids_lds[i];
-      offw[i] = (uint64_t)rows_lds[i] * (uint64_t)D;
-    }
-    if (c == 0 && tid == 0) a.ws_counts[r] = total;
-  }
-
   // --------------------------------------------------------------- 4. merge
   // A PV lane holds O^T rows d = 16*(jbase + j) + 4*g + i for head li of
   // group x.
   auto store_out = [&](int x, const f32x4* o, float lsum) {
     const int hx = hb * a.heads_per_block + x * 16 + li;
     if (hx >= a.H) return;
-    const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
+    const float inv = sticky_bad ? __builtin_nanf("") : (lsum > 0.f ? a.v_scale / lsum : 0.f);
     uint16_t* orow = a.out + ((size_t)r * a.H + hx) * D;
 #pragma unroll
     for (int j = 0; j < kCB; ++j) {
@@ -1037,22 +1043,29 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < kCB; ++j) own[((pw * kGroups + x) * kCB + j) * kWave + lane] = O[x][j];
   if (tid == 0) {
-    constexpr int kMaxSpins = 1 << 24;
-    int spins = 0;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
     while (__hip_atomic_load(published, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               a.chunks - 1 &&
-           spins < kMaxSpins) {
+           a.chunks - 1) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kMergeWaitTicks) {
+        ok = false;
+        break;
+      }
       __builtin_amdgcn_s_sleep(2);
-      ++spins;
     }
-    flag_sh = spins < kMaxSpins ? 2 : 3;
-    // every other chunk has counted itself in and published: reset for the
-    // next launch
+    flag_sh = ok ? 2 : 3;
+    // Every chunk has arrived: the arrival count restarts at 0. The
+    // published count drops by the chunks-1 publishes this launch owes, so
+    // it is back at 0 once they are all in, even if some come after a
+    // timed-out wait. A timeout also marks the workspace, so that every
+    // later launch on it is poisoned until it is zeroed again.
     __hip_atomic_store(arrived, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(published, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(published, -(a.chunks - 1), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (!ok) __hip_atomic_store(a.ws_status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  const float poison = flag_sh == 2 ? 0.f : __builtin_nanf("");
+  const float poison = flag_sh == 2 && !sticky_bad ? 0.f : __builtin_nanf("");
   // Wave w merges units (group x, column block j) half*kU .. half*kU + kU - 1
   // of PV wave src = w % kPVWaves's register order (unit = x * kCB + j).
   constexpr int kU = kGroups * kCB / 2;
@@ -1263,9 +1276,11 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   da.seq_lens = seq_lens;
   da.sel = sel_indices;
   da.out = (uint16_t*)out;
-  da.ws_ids = (int32_t*)(ws + plan->ws.ids);
-  da.ws_offsets = (uint64_t*)(ws + plan->ws.offsets);
-  da.ws_counts = (int32_t*)(ws + plan->ws.counts);
+  da.export_sel = (p.flags & DSA_DECODE_FLAG_EXPORT_SELECTION) != 0;
+  da.ws_status = (int32_t*)(ws + plan->ws.status);
+  da.ws_ids = da.export_sel ? (int32_t*)(ws + plan->ws.ids) : nullptr;
+  da.ws_offsets = da.export_sel ? (uint64_t*)(ws + plan->ws.offsets) : nullptr;
+  da.ws_counts = da.export_sel ? (int32_t*)(ws + plan->ws.counts) : nullptr;
   da.ws_arrivals = (int32_t*)(ws + plan->ws.arrivals);
   da.part_o = plan->chunks > 1 ? (float*)(ws + plan->ws.part_o) : nullptr;
   da.part_ml = plan->chunks > 1 ? (float*)(ws + plan->ws.part_ml) : nullptr;
@@ -1314,6 +1329,10 @@ int dsa_decode_read_selection(dsa_decode_plan_t plan, const void* workspace,
   if (st != DSA_DECODE_OK) return st;
   if (workspace_bytes < plan->ws.total)
     return fail(DSA_DECODE_ERR_WORKSPACE, "dsa_decode_read_selection: workspace too small");
+  if (!(plan->p.flags & DSA_DECODE_FLAG_EXPORT_SELECTION))
+    return fail(DSA_DECODE_ERR_INVALID,
+                "dsa_decode_read_selection: the plan was made without "
+                "DSA_DECODE_FLAG_EXPORT_SELECTION, so launches do not export the selection");
   const uint8_t* ws = (const uint8_t*)workspace;
   const size_t RW = (size_t)plan->p.num_rows * plan->p.sel_width;
   const hipStream_t s = (hipStream_t)stream;

@@ -134,6 +134,15 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
   for (int i = 0; i < 2; ++i)
     if (p->reserved[i] != 0)
       return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
+  if ((p->flags & ~DSA_DECODE_FLAG_EXPORT_SELECTION) != 0) {
+    m << "dsa_decode_plan: unknown flags 0x" << std::hex << p->flags;
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  if (p->qk_rope_dim != 0) {
+    m << "dsa_decode_plan: qk_rope_dim " << p->qk_rope_dim
+      << " is not compiled in (supported: 0)";
+    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
+  }
   if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS16) {
     m << "dsa_decode_plan: layout " << p->layout
       << " is not 0 (auto), 1 (32-head blocks) or 2 (16-head blocks)";
@@ -209,14 +218,18 @@ void plan_layout(dsa_decode_plan_s* plan) {
 
   WorkspaceLayout& L = plan->ws;
   size_t off = 0;
-  L.ids = off;
-  off = align_up(off + sizeof(int32_t) * R * W, kWsAlign);
-  L.offsets = off;
-  off = align_up(off + sizeof(uint64_t) * R * W, kWsAlign);
-  L.counts = off;
-  off = align_up(off + sizeof(int32_t) * R, kWsAlign);
+  L.status = off;
+  off = align_up(off + sizeof(int32_t), kWsAlign);
   L.arrivals = off;
   off = align_up(off + sizeof(int32_t) * 2 * R * plan->head_blocks, kWsAlign);
+  if (p.flags & DSA_DECODE_FLAG_EXPORT_SELECTION) {
+    L.ids = off;
+    off = align_up(off + sizeof(int32_t) * R * W, kWsAlign);
+    L.offsets = off;
+    off = align_up(off + sizeof(uint64_t) * R * W, kWsAlign);
+    L.counts = off;
+    off = align_up(off + sizeof(int32_t) * R, kWsAlign);
+  }
   if (plan->chunks > 1) {
     // Partials are kept per workgroup for a full block of heads_per_block
     // heads (a block that holds fewer heads still stores whole head groups).
@@ -321,6 +334,10 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->heads_per_block = plan->heads_per_block;
   info->rows_per_sequence = plan->p.rows_per_sequence > 1 ? plan->p.rows_per_sequence : 1;
   info->workspace_bytes = plan->ws.total;
+  info->flags = plan->p.flags;
+  info->qk_rope_dim = plan->p.qk_rope_dim;
+  info->status_offset = plan->ws.status;
+  info->counters_offset = plan->ws.arrivals;
   return DSA_DECODE_OK;
 }
 

@@ -24,10 +24,11 @@ constexpr int kHeadsPerSmallBlock = 16;
 constexpr size_t kWsAlign = 256;
 
 struct WorkspaceLayout {
-  size_t ids = 0;       // int32 [R, W]
-  size_t offsets = 0;   // uint64 [R, W]
-  size_t counts = 0;    // int32 [R]
+  size_t status = 0;    // int32: 0 healthy, 1 after a split merge gave up waiting (sticky)
   size_t arrivals = 0;  // int32 [2, R, head_blocks] arrived / published counts (zero between launches)
+  size_t ids = 0;       // int32 [R, W]  (DSA_DECODE_FLAG_EXPORT_SELECTION only)
+  size_t offsets = 0;   // uint64 [R, W] (DSA_DECODE_FLAG_EXPORT_SELECTION only)
+  size_t counts = 0;    // int32 [R]     (DSA_DECODE_FLAG_EXPORT_SELECTION only)
   size_t part_o = 0;    // float [R, head_blocks, C, heads_per_block, D] (C > 1 only)
   size_t part_ml = 0;   // float [R, head_blocks, C, heads_per_block, 2] (C > 1 only)
   size_t total = 0;

@@ -118,6 +118,7 @@ int main(void) {
   p.block_table_stride = STRIDE;
   p.max_seq_len = MAXLEN;
   p.sm_scale = sm_scale;
+  p.flags = DSA_DECODE_FLAG_EXPORT_SELECTION;
   dsa_decode_plan_t plan = NULL;
   if (dsa_decode_plan(&p, 0, &plan) != DSA_DECODE_OK) {
     fprintf(stderr, "plan: %s\n", dsa_decode_last_error());

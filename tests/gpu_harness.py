@@ -39,7 +39,8 @@ class GpuRun:
 
 
 def plan_for(wl: WL.Workload, chunk_tokens: int = 0, max_seq_len=None,
-             layout: int = 0, rows_per_sequence: int = 0) -> dsa.Plan:
+             layout: int = 0, rows_per_sequence: int = 0,
+             export_selection: bool = False) -> dsa.Plan:
     return dsa.Plan(num_rows=wl.rows, num_q_heads=wl.heads, kv_lora_rank=wl.D,
                     block_size=wl.block_size, index_kpool=wl.kpool,
                     sel_width=wl.width, block_table_stride=wl.bt_stride,
@@ -48,6 +49,7 @@ def plan_for(wl: WL.Workload, chunk_tokens: int = 0, max_seq_len=None,
                     cache_stride_bytes=wl.cache_stride_bytes,
                     chunk_tokens=chunk_tokens, layout=layout,
                     rows_per_sequence=rows_per_sequence,
+                    export_selection=export_selection,
                     device=torch.cuda.current_device())
 
 
@@ -67,7 +69,7 @@ def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
     s = i32(sl_)
     out = torch.full_like(q, float("nan"))
     plan = plan_for(wl, chunk_tokens, max_seq_len=max_seq_len, layout=layout,
-                    rows_per_sequence=rows_per_sequence)
+                    rows_per_sequence=rows_per_sequence, export_selection=with_selection)
     ws = plan.new_workspace()
     plan.launch(q, k_pool, v_pool, bt, sl, s, wl.k_scale, wl.v_scale, out, ws)
     ids = counts = offs = None

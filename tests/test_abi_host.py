@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(native):
 
 
 def test_version(native):
-    assert native.lib().dsa_decode_version() == 302
+    assert native.lib().dsa_decode_version() == 400
 
 
 def plan(native, **kw):
@@ -165,14 +165,21 @@ def test_chunk_lead(native):
 
 
 def test_workspace_layout(native):
-    p = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128)
     R, W, C, HB, HPB, D = 32, 2048, 4, 2, 32, 512
-    need = (R * W * 4 + R * W * 8 + R * 4 + 2 * R * HB * 4 + R * HB * C * HPB * D * 4
-            + R * HB * C * HPB * 2 * 4)
-    assert need <= p.workspace_bytes <= need + 6 * 256
+    core = 4 + 2 * R * HB * 4 + R * HB * C * HPB * D * 4 + R * HB * C * HPB * 2 * 4
+    export = R * W * 4 + R * W * 8 + R * 4
+    for flag, need in ((False, core), (True, core + export)):
+        p = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128,
+                 export_selection=flag)
+        assert need <= p.workspace_bytes <= need + 7 * 256
+        info = p.info()
+        assert info["flags"] == (1 if flag else 0)
+        assert info["status_offset"] == 0 and info["counters_offset"] == 256
     p1 = plan(native)
-    assert p1.info()["chunks_per_row"] == 1        # no partials
-    assert p1.workspace_bytes <= 128 * 2048 * 12 + 128 * 12 + 4 * 256
+    assert p1.info()["chunks_per_row"] == 1        # no partials, no export
+    assert p1.workspace_bytes <= 4 * 256 + 2 * 128 * 2 * 4
+    p2 = plan(native, export_selection=True)
+    assert p2.workspace_bytes <= 128 * 2048 * 12 + 128 * 12 + 6 * 256
 
 
 def test_head_blocks(native):
@@ -325,7 +332,7 @@ def test_planner_invariants_over_random_geometries(native):
     row table exceeds its 2048 LDS entries, the grid covers every (row,
     chunk, head block) unit in whole rounds of 8 (whole blocks of 8
     sequences when rows are co-scheduled), and the workspace holds the
-    exported selection plus, when rows are split, every partial."""
+    status word and counters plus, when rows are split, every partial."""
     from hypothesis import given, settings, strategies as st
 
     @settings(max_examples=300, deadline=None)
@@ -361,11 +368,12 @@ def test_planner_invariants_over_random_geometries(native):
         else:
             assert info["workgroups"] == -(-units // 8) * 8 * HB
         assert info["workgroups"] >= units * HB
-        need = rows * width * 12 + rows * 4 + 2 * rows * HB * 4
+        need = 4 + 2 * rows * HB * 4                 # status word and counters
         if C > 1:
             slots = rows * HB * C * info["heads_per_block"]
             need += slots * D * 4 + slots * 2 * 4
         assert need <= p.workspace_bytes <= need + 8 * 256
+        assert p.info()["counters_offset"] >= 4
         p.close()
 
     check()

@@ -115,6 +115,20 @@ def test_writer_small_batches(H, rows, D):
     assert ties <= 2
 
 
+@pytest.mark.parametrize("sigma,eps", [(2.0 ** -10, 2.0 ** -20), (2.0 ** -8, 3.0 * 2.0 ** -16),
+                                       (1e-3, 1e-5)])
+def test_writer_eps_comparable_to_mean_square(H, sigma, eps):
+    """Rows whose mean square is of the order of rms_eps, so that where eps
+    enters the root changes every code: the GPU writer must match the
+    oracle's placement (inside the root, unscaled)."""
+    rng = np.random.default_rng(int(1e6 * sigma) + 5)
+    _announce("latent_write eps", sigma=sigma, eps=eps)
+    ties, n, host, got, values = _run_case(H, rng, rows=65, D=512, B=64, pages=4,
+                                           stride_pad=0, sigma=sigma, inv=1 / 0.02, eps=eps)
+    # (mean square / (mean square + eps) is about 1/2, 1/4 and 1/11 here)
+    assert ties <= 2
+
+
 def test_writer_saturates(H):
     rng = np.random.default_rng(9)
     _announce("latent_write saturation")

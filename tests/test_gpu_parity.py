@@ -445,6 +445,60 @@ def test_many_chunk_merges_repeated_on_one_workspace(H, layout):
     plan.close()
 
 
+def test_timed_out_merge_poisons_the_workspace_until_reinit(H):
+    """The split merge's bounded wait, forced from the host: the published
+    count of one (row, head block) is preset far below zero, so its merger
+    gives up after its time limit while every kernel still ends normally.
+    That block's output must be NaN and the rest correct; the workspace's
+    status word then poisons every later launch on it, until
+    dsa_decode_workspace_init zeroes it, after which the output is right
+    again."""
+    rng = np.random.default_rng(78)
+    wl = WL.random_case(rng, rows=4, heads=64, D=512, block_size=64, max_len=3000,
+                        width=2048)
+    _announce("timed-out merge, sticky status")
+    plan = H.plan_for(wl, chunk_tokens=512, layout=1)
+    info = plan.info()
+    R, HB, C = wl.rows, info["head_blocks"], info["chunks_per_row"]
+    assert C >= 2 and HB == 2
+    q, pool = H.q_tensor(wl.q_bits), H.u8(wl.pool)
+    bt, sl, sel = H.i32(wl.block_tables), H.i32(wl.seq_lens), H.i32(wl.sel)
+    ws = plan.new_workspace()
+    counters = ws.narrow(0, info["counters_offset"], 8 * R * HB).view(torch.int32)
+    status = ws.narrow(0, info["status_offset"], 4).view(torch.int32)
+    bad_row, bad_hb = 1, 1
+    counters[R * HB + bad_row * HB + bad_hb] = -(1 << 30)
+
+    def launch():
+        out = torch.full_like(q, float("nan"))
+        plan.launch(q, pool, pool, bt, sl, sel, wl.k_scale, wl.v_scale, out, ws)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64)
+
+    want = H.oracle_rows(wl, range(R))
+    first = launch()
+    bad = np.zeros((R, wl.heads), dtype=bool)
+    bad[bad_row, 32 * bad_hb:32 * (bad_hb + 1)] = True
+    assert np.isnan(first[bad]).all()
+    assert np.isfinite(first[~bad]).all()
+    err = H.normwise_err(np.where(bad[..., None], want, first), want)
+    assert err.max() <= H.TOL
+    assert int(status.item()) == 1
+    c = counters.cpu().numpy()
+    assert (c[:R * HB] == 0).all()                                   # arrivals reset
+    assert c[R * HB + bad_row * HB + bad_hb] == -(1 << 30)           # publishes owed came in
+    assert (np.delete(c[R * HB:], bad_row * HB + bad_hb) == 0).all()
+    second = launch()
+    assert np.isnan(second).all(), "a poisoned workspace must poison every output"
+    plan.workspace_init(ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    third = launch()
+    assert np.isfinite(third).all()
+    assert H.normwise_err(third, want).max() <= H.TOL
+    plan.close()
+
+
 # ------------------------------------------------------------ launch errors
 
 def test_launch_rejects_bad_arguments(H):
@@ -484,6 +538,11 @@ def test_launch_rejects_bad_arguments(H):
     # nothing was launched: out is untouched by the refused calls
     plan.launch(q, pool, pool, bt, sl, sel, 0.05, 0.05, out, ws)
     torch.cuda.synchronize()
+    # the read-back hook needs a plan that exports the selection
+    with pytest.raises(dsa.DsaDecodeError) as e:
+        plan.read_selection(ws, counts=torch.empty(2, dtype=torch.int32, device=q.device))
+    assert e.value.status == dsa.DSA_DECODE_ERR_INVALID
+    assert "EXPORT_SELECTION" in str(e.value)
 
 
 def test_plan_on_gfx950_device(H):
