@@ -239,6 +239,27 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q,
                       void* out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* dsa_decode_launch without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. It allocates nothing (no hipMalloc, no
+ * allocating library call): the workspace is a static device array of the
+ * library, 32 MiB, one copy on every GPU the library runs on, held until the
+ * process ends (its address is looked up once per device). Before the decode
+ * it clears the status word and the arrival counters with a fill kernel on
+ * `stream` (the array keeps whatever the last call on the GPU left in it);
+ * the split partials need no clearing. Arguments, results and asynchrony as
+ * for dsa_decode_launch. Calls that overlap on one GPU (other streams, other
+ * threads, graphs replayed concurrently) share the array and race: serialise
+ * them. Errors as for dsa_decode_launch, plus DSA_DECODE_ERR_WORKSPACE when
+ * the plan's workspace (dsa_decode_workspace_bytes) exceeds 32 MiB, and
+ * DSA_DECODE_ERR_INVALID for a plan with DSA_DECODE_FLAG_EXPORT_SELECTION
+ * (the export is read back from a caller workspace). */
+int dsa_decode_launch_static(dsa_decode_plan_t plan, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             const int32_t* sel_indices, float k_scale,
+                             float v_scale, void* out, void* stream);
+
 /* Copy the normalised selection the last launch on `workspace` computed
  * (what the attention consumed) into caller device memory, on `stream`.
  * Only for plans made with DSA_DECODE_FLAG_EXPORT_SELECTION (otherwise

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "dsa_decode_workspace_init", "dsa_decode_plan_get_info", "dsa_decode_launch", "dsa_decode_read_selection",
     "dsa_decode_timing_begin", "dsa_decode_timing_end", "dsa_decode_last_error",
     "dsa_decode_version", "dsa_decode_latent_write", "dsa_decode_masked_reference",
+    "dsa_decode_launch_static",
 )
 
 
@@ -121,6 +122,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_decode_launch.restype = ctypes.c_int
         L.dsa_decode_launch.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
                                         ctypes.c_float, vp, vp, sz, vp]
+        L.dsa_decode_launch_static.restype = ctypes.c_int
+        L.dsa_decode_launch_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float,
+                                               ctypes.c_float, vp, vp]
         L.dsa_decode_read_selection.restype = ctypes.c_int
         L.dsa_decode_read_selection.argtypes = [vp, vp, sz, vp, vp, vp, vp]
         L.dsa_decode_timing_begin.restype = ctypes.c_int
@@ -238,6 +242,15 @@ class Plan:
             self.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
             _ptr(seq_lens), _ptr(sel_indices), float(k_scale), float(v_scale),
             _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+    def launch_static(self, q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
+                      k_scale: float, v_scale: float, out, stream=None) -> None:
+        """dsa_decode_launch_static: the decode with the library's static
+        scratch instead of a caller workspace (allocates nothing)."""
+        _check(self._lib.dsa_decode_launch_static(
+            self.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(seq_lens), _ptr(sel_indices), float(k_scale), float(v_scale),
+            _ptr(out), _stream(stream)))
 
     def read_selection(self, workspace, ids=None, counts=None, offsets=None,
                        workspace_bytes=None, stream=None) -> None:

@@ -48,6 +48,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <sstream>
 
 #include "plan.hpp"
@@ -1150,6 +1151,13 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
 }
 
+// Scratch of the entry point that allocates nothing (dsa_decode_launch_static):
+// the decode's workspace (status word, arrival counters, split partials) for
+// callers that cannot allocate device memory. Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 // Zero a word range (workspace set-up; a kernel rather than a memset so that
 // it can sit in a captured graph).
 __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
@@ -1205,6 +1213,61 @@ int check_device(dsa_decode_plan_t plan, const char* who) {
   return DSA_DECODE_OK;
 }
 
+int check_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                 const int32_t* sel_indices, float k_scale, float v_scale, const void* out,
+                 const char* who) {
+  if (!plan) return fail(DSA_DECODE_ERR_INVALID, std::string(who) + ": plan is NULL");
+  int st = check_device(plan, who);
+  if (st != DSA_DECODE_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !sel_indices || !out)
+    return fail(DSA_DECODE_ERR_INVALID, std::string(who) + ": NULL device pointer");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(DSA_DECODE_ERR_INVALID,
+                std::string(who) + ": q, out, k_cache and v_cache must be 16-byte aligned");
+  if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale)) {
+    std::ostringstream m;
+    m << who << ": k_scale must be finite and > 0 and v_scale finite (got " << k_scale
+      << ", " << v_scale << ")";
+    return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  return DSA_DECODE_OK;
+}
+
+int enqueue_decode(dsa_decode_plan_t plan, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                   const int32_t* sel_indices, float k_scale, float v_scale, void* out,
+                   void* workspace, hipStream_t stream_h, const char* who);
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept. In host code the array's name
+// is only a stand-in for the symbol, never a device address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(int device, void** out, const char* who) {
+  if (device < 0 || device >= kMaxDevices) {
+    std::ostringstream m;
+    m << who << ": device " << device << " is beyond the " << kMaxDevices
+      << " devices the static scratch table covers";
+    return fail(DSA_DECODE_ERR_DEVICE, m.str());
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(DSA_DECODE_ERR_DEVICE, std::string(who) + ": hipGetSymbolAddress(scratch): " +
+                                             hipGetErrorString(e));
+    }
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return DSA_DECODE_OK;
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -1242,25 +1305,64 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
                       float k_scale, float v_scale, void* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
   using namespace dsa;
-  if (!plan) return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_launch: plan is NULL");
-  int st = check_device(plan, "dsa_decode_launch");
+  int st = check_launch(plan, q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
+                        k_scale, v_scale, out, "dsa_decode_launch");
   if (st != DSA_DECODE_OK) return st;
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !sel_indices || !out)
-    return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_launch: NULL device pointer");
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
-    return fail(DSA_DECODE_ERR_INVALID,
-                "dsa_decode_launch: q, out, k_cache and v_cache must be 16-byte aligned");
-  if (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale)) {
-    std::ostringstream m;
-    m << "dsa_decode_launch: k_scale must be finite and > 0 and v_scale finite (got "
-      << k_scale << ", " << v_scale << ")";
-    return fail(DSA_DECODE_ERR_INVALID, m.str());
-  }
   st = check_workspace(plan, workspace, workspace_bytes, "dsa_decode_launch");
   if (st != DSA_DECODE_OK) return st;
+  return enqueue_decode(plan, q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
+                        k_scale, v_scale, out, workspace, (hipStream_t)stream,
+                        "dsa_decode_launch");
+}
 
+int dsa_decode_launch_static(dsa_decode_plan_t plan, const void* q, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables,
+                             const int32_t* seq_lens, const int32_t* sel_indices,
+                             float k_scale, float v_scale, void* out, void* stream) {
+  using namespace dsa;
+  const char* who = "dsa_decode_launch_static";
+  int st = check_launch(plan, q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
+                        k_scale, v_scale, out, who);
+  if (st != DSA_DECODE_OK) return st;
+  if (plan->p.flags & DSA_DECODE_FLAG_EXPORT_SELECTION)
+    return fail(DSA_DECODE_ERR_INVALID,
+                std::string(who) + ": the selection export is read back from a caller "
+                "workspace; make the plan without DSA_DECODE_FLAG_EXPORT_SELECTION");
+  if (plan->ws.total > kStaticScratchBytes) {
+    std::ostringstream m;
+    m << who << ": the plan needs " << plan->ws.total
+      << " bytes of scratch, more than the library's static " << kStaticScratchBytes
+      << " bytes; use dsa_decode_launch with a workspace";
+    return fail(DSA_DECODE_ERR_WORKSPACE, m.str());
+  }
+  void* ws = nullptr;
+  st = static_scratch(plan->device, &ws, who);
+  if (st != DSA_DECODE_OK) return st;
+  // The scratch keeps whatever the last call on this device left in it. The
+  // status word and the arrival counters must start at zero: cleared by a
+  // fill kernel (not a memset, so the call can be captured in a graph).
+  const hipStream_t s = (hipStream_t)stream;
+  const size_t words = (plan->ws.arrivals + sizeof(int32_t) * 2 * (size_t)plan->p.num_rows *
+                        (size_t)plan->head_blocks) / sizeof(int32_t);
+  hipLaunchKernelGGL(dsa_zero_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 1024)),
+                     dim3(256), 0, s, (int32_t*)ws, words);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(DSA_DECODE_ERR_LAUNCH, std::string(who) + ": " + hipGetErrorString(e));
+  return enqueue_decode(plan, q, k_cache, v_cache, block_tables, seq_lens, sel_indices,
+                        k_scale, v_scale, out, ws, s, who);
+}
+
+}  // extern "C"
+
+namespace dsa {
+namespace {
+
+int enqueue_decode(dsa_decode_plan_t plan, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                   const int32_t* sel_indices, float k_scale, float v_scale, void* out,
+                   void* workspace, hipStream_t stream_h, const char* who) {
   const dsa_decode_params& p = plan->p;
-  const hipStream_t stream_h = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
 
   hipEvent_t* ev = nullptr;
@@ -1314,10 +1416,15 @@ int dsa_decode_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,
-                std::string("dsa_decode_launch: decode kernel: ") + hipGetErrorString(e));
+                std::string(who) + ": decode kernel: " + hipGetErrorString(e));
   if (ev) (void)hipEventRecord(ev[1], stream_h);
   return DSA_DECODE_OK;
 }
+
+}  // namespace
+}  // namespace dsa
+
+extern "C" {
 
 int dsa_decode_read_selection(dsa_decode_plan_t plan, const void* workspace,
                               size_t workspace_bytes, int32_t* ids, int32_t* counts,
