@@ -52,6 +52,9 @@ def parse():
                     help="also run one plain device copy of this many MiB "
                          "(reference dispatch for HBM counter calibration)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--merge-in-kernel", action="store_true",
+                    help="split rows merged by their last chunk inside the decode "
+                         "kernel instead of by the combine kernel")
     ap.add_argument("--rows-per-sequence", type=int, default=-1,
                     help="decode_k rows per sequence co-scheduled on one XCD "
                          "(-1: the workload's own, 4 for verify, else 1)")
@@ -110,7 +113,7 @@ def main():
                     block_size=base.block_size, index_kpool=base.kpool, sel_width=W,
                     block_table_stride=base.bt_stride, max_seq_len=base.max_seq_len,
                     sm_scale=base.sm_scale, cache_stride_bytes=base.cache_stride_bytes,
-                    chunk_tokens=args.chunk_tokens,
+                    chunk_tokens=args.chunk_tokens, merge_in_kernel=args.merge_in_kernel,
                     rows_per_sequence=rows_per_seq, device=0)
     ws = plan.new_workspace(0)
     info = plan.info()

@@ -129,6 +129,11 @@ typedef struct dsa_decode_params {
  * default: the decode itself never needs it, and it costs 12 bytes of
  * workspace and of HBM writes per selection slot. */
 #define DSA_DECODE_FLAG_EXPORT_SELECTION 1
+/* flags: split rows (chunks_per_row > 1) are merged inside the decode kernel
+ * by the last chunk of each (row, head block) to finish, which waits for the
+ * others' partials, instead of by a separate combine kernel over every CU
+ * (the default). The result is the same either way. */
+#define DSA_DECODE_FLAG_MERGE_IN_KERNEL 2
 
 /* Opaque plan: validated geometry plus the launch decomposition. Host
  * memory owned by the library; free it with dsa_decode_plan_destroy. */
@@ -143,12 +148,15 @@ typedef struct dsa_decode_plan_info {
   int32_t workgroups;      /* launched: rows * chunks_per_row rounded up to
                             * a multiple of 8 (of 8 * rows_per_sequence when
                             * rows are co-scheduled), times head_blocks */
-  int32_t merges_chunks;   /* 1 when chunks_per_row > 1: the last chunk of a
-                            * row to finish merges the others' partials */
+  int32_t merges_chunks;   /* 0: rows are not split; 1: split rows are merged
+                            * by a separate combine kernel (a second launch on
+                            * the same stream); 2: by the last chunk of a row
+                            * to finish, inside the decode kernel
+                            * (DSA_DECODE_FLAG_MERGE_IN_KERNEL) */
   int32_t num_cus;         /* compute units the plan was sized for */
-  int32_t chunk_lead;      /* extra selected tokens of chunk 0 when split (it
-                            * finishes last and merges); the last chunk has
-                            * that many fewer */
+  int32_t chunk_lead;      /* extra selected tokens of chunk 0 when split rows
+                            * are merged in the kernel (it then finishes last
+                            * and merges); the last chunk has that many fewer */
   uint64_t workspace_bytes;
   int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32 or _HEADS16 (resolved) */
   int32_t heads_per_block; /* 32 or 16 */

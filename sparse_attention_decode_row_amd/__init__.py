@@ -29,6 +29,7 @@ DSA_DECODE_ERR_WORKSPACE = -4
 DSA_DECODE_ERR_LAUNCH = -5
 
 DSA_DECODE_FLAG_EXPORT_SELECTION = 1
+DSA_DECODE_FLAG_MERGE_IN_KERNEL = 2
 
 EXPORTED_SYMBOLS = (
     "dsa_decode_plan", "dsa_decode_plan_destroy", "dsa_decode_workspace_bytes",
@@ -176,21 +177,24 @@ def _stream(stream) -> Optional[int]:
 class Plan:
     """A validated decode geometry (dsa_decode_plan). device=-1 builds a
     host-only plan (validation and sizing, no launches). export_selection
-    sets DSA_DECODE_FLAG_EXPORT_SELECTION (needed by read_selection)."""
+    sets DSA_DECODE_FLAG_EXPORT_SELECTION (needed by read_selection),
+    merge_in_kernel DSA_DECODE_FLAG_MERGE_IN_KERNEL."""
 
     def __init__(self, *, num_rows: int, num_q_heads: int, kv_lora_rank: int,
                  block_size: int, index_kpool: int, sel_width: int,
                  block_table_stride: int, max_seq_len: int, sm_scale: float,
                  num_kv_heads: int = 1, cache_stride_bytes: int = 0,
                  chunk_tokens: int = 0, layout: int = 0, rows_per_sequence: int = 0,
-                 export_selection: bool = False, flags: int = 0, qk_rope_dim: int = 0,
-                 device: Optional[int] = None):
+                 export_selection: bool = False, merge_in_kernel: bool = False,
+                 flags: int = 0, qk_rope_dim: int = 0, device: Optional[int] = None):
         if device is None:
             import torch
             device = torch.cuda.current_device()
         self._lib = lib()
         if export_selection:
             flags |= DSA_DECODE_FLAG_EXPORT_SELECTION
+        if merge_in_kernel:
+            flags |= DSA_DECODE_FLAG_MERGE_IN_KERNEL
         self.params = Params(num_rows, num_q_heads, num_kv_heads, kv_lora_rank,
                              block_size, index_kpool, sel_width, block_table_stride,
                              cache_stride_bytes, max_seq_len, sm_scale, chunk_tokens,

@@ -57,6 +57,7 @@ namespace dsa {
 namespace {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -281,6 +282,7 @@ struct DecodeArgs {
   float scale_log2;  // sm_scale * k_scale * log2(e), > 0
   float v_scale;
   int export_sel;    // write the selection (ids, offsets, counts) for the read-back hook
+  int merge_in_kernel;  // split rows: 1 the last chunk merges, 0 every chunk publishes for the combine kernel
 };
 
 // Longest a merging workgroup waits for the other chunks' partials, in ticks
@@ -1011,6 +1013,34 @@ void dsa_decode_kernel(DecodeArgs a) {
   auto part_ml_of = [&](int cc, int x) {
     return a.part_ml + ((wg_slot + cc) * a.heads_per_block + x * 16 + li) * 2;
   };
+  if (!a.merge_in_kernel) {
+    // Every chunk publishes; the combine kernel, launched next on the same
+    // stream, merges them (the kernel boundary orders the stores). The
+    // partial is stored normalised by the chunk's own weight sum, as fp16:
+    // a weighted mean of FP8 codes, so |o / l| <= 448, with a relative
+    // error of at most 2^-11 per element.
+    if (!is_qk) {
+      _Float16* po = (_Float16*)part_o_of(c, pw);
+#pragma unroll
+      for (int x = 0; x < kGroups; ++x) {
+        const float il = l_run[x] > 0.f ? 1.f / l_run[x] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) {
+          const f16x4 h = {(_Float16)(O[x][j][0] * il), (_Float16)(O[x][j][1] * il),
+                           (_Float16)(O[x][j][2] * il), (_Float16)(O[x][j][3] * il)};
+          *(f16x4*)(po + ((x * kCB + j) * kWave + lane) * 4) = h;
+        }
+      }
+      if (pw == 0 && g == 0)
+#pragma unroll
+        for (int x = 0; x < kGroups; ++x) {
+          float* pml = part_ml_of(c, x);
+          pml[0] = m_run[x];
+          pml[1] = l_run[x];
+        }
+    }
+    return;
+  }
   if (tid == 0) flag_sh = atomicAdd(arrived, 1) == a.chunks - 1 ? 2 : 0;
   __syncthreads();
   if (flag_sh != 2) {
@@ -1158,6 +1188,62 @@ void dsa_decode_kernel(DecodeArgs a) {
 constexpr size_t kStaticScratchBytes = size_t(32) << 20;
 __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
+// Merge of split rows ([attend], the split softmax and its combine), one
+// thread per 4 output columns of one head. Every chunk c of (row r, head
+// block hb) left its accumulators normalised by its weight sum, a_c = o_c /
+// l_c (fp16, in its PV waves' register order), its reference m_c (log2
+// domain) and l_c; with M = max_c m_c and w_c = 2^(m_c - M) l_c the output is
+//   out = v_scale * sum_c w_c a_c / sum_c w_c
+// (0 when every chunk is empty), the chunks taken in order. Thread t of a
+// (row, head block) reads element group t of each chunk's partial: in the
+// register order that is PV wave src, head group x, column block j, lane
+// (head li, column quarter g), the layout the decode kernel stores.
+template <int D, int kGroups>
+__global__ __launch_bounds__(256)
+void dsa_combine_kernel(DecodeArgs a) {
+  constexpr int kPVWaves = kParts * kGroups;
+  constexpr int kCB = D / 16 / kPVWaves;
+  constexpr int kUnits = kPVWaves * kGroups * kCB * kWave;  // float4s per chunk partial
+  constexpr int kBlocksPerUnit = kUnits / 256;
+  static_assert(kUnits % 256 == 0, "whole blocks per (row, head block)");
+  const int rh = blockIdx.x / kBlocksPerUnit;  // r * head_blocks + hb
+  const int t = (blockIdx.x % kBlocksPerUnit) * 256 + threadIdx.x;
+  if (rh >= a.rows * a.head_blocks) return;
+  const int r = rh / a.head_blocks, hb = rh % a.head_blocks;
+  const int lane = t % kWave, li = lane & 15, g = lane >> 4;
+  const int j = (t / kWave) % kCB, x = (t / (kWave * kCB)) % kGroups;
+  const int src = t / (kWave * kCB * kGroups);
+  const int hx = hb * a.heads_per_block + x * 16 + li;
+  if (hx >= a.H) return;
+  const size_t slot0 = (size_t)rh * a.chunks;
+  const float* ml = a.part_ml + (slot0 * a.heads_per_block + x * 16 + li) * 2;
+  const size_t ml_stride = (size_t)a.heads_per_block * 2;
+  float M = -INFINITY;
+  for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, ml[c * ml_stride]);
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  // Each chunk keeps an fp32-sized slot of kUnits * 4 floats, one
+  // kPartFloats region per PV wave; the fp16 partial fills the first half
+  // of its wave's region, 4 halves per (group, block, lane) unit u.
+  constexpr int kPartFloats = kGroups * kCB * kWave * 4;
+  const int u = t % (kGroups * kCB * kWave);
+  const _Float16* p0 = (const _Float16*)(a.part_o + slot0 * kUnits * 4 + src * kPartFloats) + u * 4;
+  constexpr size_t kChunkHalves = (size_t)kUnits * 4 * 2;
+#pragma unroll 4
+  for (int c = 0; c < a.chunks; ++c) {
+    const float m = ml[c * ml_stride];
+    const float w = m == -INFINITY ? 0.f : fast_exp2(m - M) * ml[c * ml_stride + 1];
+    L += w;
+    const f16x4 h = *(const f16x4*)(p0 + c * kChunkHalves);
+    o += f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * w;
+  }
+  const bool bad = __hip_atomic_load(a.ws_status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+  const float inv = bad ? __builtin_nanf("") : (L > 0.f ? a.v_scale / L : 0.f);
+  const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
+                    (__bf16)(o[3] * inv)};
+  *(bf16x4*)(a.out + ((size_t)r * a.H + hx) * D + 16 * (src * kCB + j) + 4 * g) = v;
+}
+
 // Zero a word range (workspace set-up; a kernel rather than a memset so that
 // it can sit in a captured graph).
 __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
@@ -1169,19 +1255,25 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int kGroups>
-hipError_t launch_g(bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+hipError_t launch_g(bool split_v, bool combine, dim3 grid, hipStream_t st, const DecodeArgs& args) {
   const dim3 block(4 * kGroups * kWave);
   if (split_v)
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
   else
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false>), grid, block, 0, st, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !combine) return e;
+  constexpr int kUnits = D * kGroups * 4;  // float4s of one (row, head block)'s partial
+  const dim3 cgrid((unsigned)((size_t)args.rows * args.head_blocks * (kUnits / 256)));
+  hipLaunchKernelGGL((dsa_combine_kernel<D, kGroups>), cgrid, dim3(256), 0, st, args);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int groups, bool split_v, dim3 grid, hipStream_t st, const DecodeArgs& args) {
-  return groups == 1 ? launch_g<D, 1>(split_v, grid, st, args)
-                     : launch_g<D, 2>(split_v, grid, st, args);
+hipError_t launch_d(int groups, bool split_v, bool combine, dim3 grid, hipStream_t st,
+                    const DecodeArgs& args) {
+  return groups == 1 ? launch_g<D, 1>(split_v, combine, grid, st, args)
+                     : launch_g<D, 2>(split_v, combine, grid, st, args);
 }
 
 
@@ -1404,15 +1496,17 @@ int enqueue_decode(dsa_decode_plan_t plan, const void* q, const void* k_cache,
   da.group_units = plan->group_units;
   da.scale_log2 = p.sm_scale * k_scale * kLog2e;
   da.v_scale = v_scale;
+  da.merge_in_kernel = plan->merge_in_kernel ? 1 : 0;
   const int groups = plan->heads_per_block / 16;
   const bool split_v = k_cache != v_cache;
+  const bool combine = plan->chunks > 1 && !plan->merge_in_kernel;
   const dim3 grid(plan->workgroups);
   hipError_t e;
   switch (p.kv_lora_rank) {
-    case 64: e = launch_d<64>(groups, split_v, grid, stream_h, da); break;
-    case 128: e = launch_d<128>(groups, split_v, grid, stream_h, da); break;
-    case 256: e = launch_d<256>(groups, split_v, grid, stream_h, da); break;
-    default: e = launch_d<512>(groups, split_v, grid, stream_h, da); break;
+    case 64: e = launch_d<64>(groups, split_v, combine, grid, stream_h, da); break;
+    case 128: e = launch_d<128>(groups, split_v, combine, grid, stream_h, da); break;
+    case 256: e = launch_d<256>(groups, split_v, combine, grid, stream_h, da); break;
+    default: e = launch_d<512>(groups, split_v, combine, grid, stream_h, da); break;
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,

@@ -134,7 +134,7 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
   for (int i = 0; i < 2; ++i)
     if (p->reserved[i] != 0)
       return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_plan: reserved fields must be zero");
-  if ((p->flags & ~DSA_DECODE_FLAG_EXPORT_SELECTION) != 0) {
+  if ((p->flags & ~(DSA_DECODE_FLAG_EXPORT_SELECTION | DSA_DECODE_FLAG_MERGE_IN_KERNEL)) != 0) {
     m << "dsa_decode_plan: unknown flags 0x" << std::hex << p->flags;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
@@ -194,12 +194,15 @@ void plan_layout(dsa_decode_plan_s* plan) {
   plan->chunk_tokens = (int)ct;
   plan->chunks = (int)((wmax + ct - 1) / ct);
   if (plan->chunks < 1) plan->chunks = 1;
-  // With several chunks the last one to finish merges the others' partials.
-  // Giving chunk 0 one more 128-token tile (and the last chunk one fewer)
-  // makes chunk 0 that last one, so the others publish their partials while
-  // it still computes. The rank ranges still cover [0, chunks * ct).
+  // With several chunks, either a combine kernel merges every chunk's
+  // partials, or (DSA_DECODE_FLAG_MERGE_IN_KERNEL) the last chunk of a row to
+  // finish merges the others'. In the second case chunk 0 gets one more
+  // 128-token tile (and the last chunk one fewer), which makes it that last
+  // one, so the others publish their partials while it still computes. The
+  // rank ranges still cover [0, chunks * ct).
   plan->chunk_lead = 0;
-  if (plan->chunks > 1 && p.chunk_tokens == 0) {
+  plan->merge_in_kernel = (p.flags & DSA_DECODE_FLAG_MERGE_IN_KERNEL) != 0;
+  if (plan->chunks > 1 && p.chunk_tokens == 0 && plan->merge_in_kernel) {
     const int64_t lead = std::min<int64_t>(2 * kTileTokens, kMaxChunkTokens - ct);
     if (lead > 0 && ct > lead) {
       plan->chunk_lead = (int)lead;
@@ -327,7 +330,7 @@ int dsa_decode_plan_get_info(dsa_decode_plan_t plan, dsa_decode_plan_info* info)
   info->chunks_per_row = plan->chunks;
   info->head_blocks = plan->head_blocks;
   info->workgroups = plan->workgroups;
-  info->merges_chunks = plan->chunks > 1 ? 1 : 0;
+  info->merges_chunks = plan->chunks > 1 ? (plan->merge_in_kernel ? 2 : 1) : 0;
   info->num_cus = plan->num_cus;
   info->chunk_lead = plan->chunk_lead;
   info->layout = plan->layout;

@@ -43,6 +43,7 @@ struct dsa_decode_plan_s {
   int chunk_tokens = 0;           // multiple of kTileTokens, <= kMaxChunkTokens
   int chunks = 1;                 // per row per head block
   int chunk_lead = 0;             // extra tokens of chunk 0 (multiple of kTileTokens)
+  bool merge_in_kernel = false;   // split rows merged by their last chunk, not by a combine kernel
   int head_blocks = 1;
   int heads_per_block = dsa::kHeadsPerBlock;
   int layout = DSA_DECODE_LAYOUT_HEADS32;

@@ -40,7 +40,7 @@ class GpuRun:
 
 def plan_for(wl: WL.Workload, chunk_tokens: int = 0, max_seq_len=None,
              layout: int = 0, rows_per_sequence: int = 0,
-             export_selection: bool = False) -> dsa.Plan:
+             export_selection: bool = False, merge_in_kernel: bool = False) -> dsa.Plan:
     return dsa.Plan(num_rows=wl.rows, num_q_heads=wl.heads, kv_lora_rank=wl.D,
                     block_size=wl.block_size, index_kpool=wl.kpool,
                     sel_width=wl.width, block_table_stride=wl.bt_stride,
@@ -49,13 +49,14 @@ def plan_for(wl: WL.Workload, chunk_tokens: int = 0, max_seq_len=None,
                     cache_stride_bytes=wl.cache_stride_bytes,
                     chunk_tokens=chunk_tokens, layout=layout,
                     rows_per_sequence=rows_per_sequence,
-                    export_selection=export_selection,
+                    export_selection=export_selection, merge_in_kernel=merge_in_kernel,
                     device=torch.cuda.current_device())
 
 
 def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
             q_bits=None, sel=None, seq_lens=None, with_selection: bool = True,
-            max_seq_len=None, layout: int = 0, rows_per_sequence: int = 0) -> GpuRun:
+            max_seq_len=None, layout: int = 0, rows_per_sequence: int = 0,
+            merge_in_kernel: bool = False) -> GpuRun:
     """Run the decode on the GPU. k_pool / v_pool: device uint8 tensors
     (default: the workload's host pool uploaded; v_pool defaults to k_pool)."""
     if k_pool is None:
@@ -69,7 +70,8 @@ def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
     s = i32(sl_)
     out = torch.full_like(q, float("nan"))
     plan = plan_for(wl, chunk_tokens, max_seq_len=max_seq_len, layout=layout,
-                    rows_per_sequence=rows_per_sequence, export_selection=with_selection)
+                    rows_per_sequence=rows_per_sequence, export_selection=with_selection,
+                    merge_in_kernel=merge_in_kernel)
     ws = plan.new_workspace()
     plan.launch(q, k_pool, v_pool, bt, sl, s, wl.k_scale, wl.v_scale, out, ws)
     ids = counts = offs = None

@@ -153,13 +153,21 @@ def test_chunk_lead(native):
     # last and merges; a forced split keeps equal chunks
     assert plan(native).info()["chunk_lead"] == 0          # one chunk per row
     assert plan(native, chunk_tokens=192).info()["chunk_lead"] == 0
-    split = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128).info()
+    # merged by the combine kernel: equal chunks
+    comb = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128).info()
+    assert comb["chunk_tokens"] == 512 and comb["chunk_lead"] == 0
+    assert comb["chunks_per_row"] == 4 and comb["merges_chunks"] == 1
+    # merged in the kernel by chunk 0, which takes one more tile pair
+    split = plan(native, num_rows=32, max_seq_len=8192, block_table_stride=128,
+                 merge_in_kernel=True).info()
     assert split["chunk_tokens"] == 512 and split["chunk_lead"] == 128
-    small = plan(native, num_rows=8, max_seq_len=8192, block_table_stride=128).info()
+    assert split["merges_chunks"] == 2
+    small = plan(native, num_rows=8, max_seq_len=8192, block_table_stride=128,
+                 merge_in_kernel=True).info()
     assert small["chunks_per_row"] == 16 and small["chunk_tokens"] == 128
     assert small["chunk_lead"] == 0                         # a lead must be below the chunk
     # the ranges still cover every rank a row can have
-    for info in (plan(native).info(), split, small):
+    for info in (plan(native).info(), comb, split, small):
         assert info["chunks_per_row"] * info["chunk_tokens"] + info["chunk_lead"] >= 2048
         assert info["chunk_tokens"] + info["chunk_lead"] <= 2048
 

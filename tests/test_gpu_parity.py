@@ -43,11 +43,13 @@ def test_tiny(H):
     assert err.max() <= H.TOL
 
 
-def test_glm_full(H):
+@pytest.mark.parametrize("in_kernel", [False, True])
+def test_glm_full(H, in_kernel):
     wl = WL.make("glm")
-    _announce("glm", rows=wl.rows, heads=wl.heads, D=wl.D, W=wl.width)
-    run = H.run_gpu(wl)
+    _announce("glm", rows=wl.rows, heads=wl.heads, D=wl.D, W=wl.width, in_kernel=in_kernel)
+    run = H.run_gpu(wl, merge_in_kernel=in_kernel)
     print("plan", run.info)
+    assert run.info["merges_chunks"] == (2 if in_kernel else 1)
     H.check_selection(wl, run)
     want = H.oracle_rows(wl, range(wl.rows))
     err = H.normwise_err(run.out, want)
@@ -409,20 +411,22 @@ def test_deterministic(H):
     assert np.array_equal(a.out_bits, b.out_bits)
 
 
+@pytest.mark.parametrize("in_kernel", [False, True])
 @pytest.mark.parametrize("layout", [1, 2])
-def test_many_chunk_merges_repeated_on_one_workspace(H, layout):
-    """The split merge under load: 64-token chunks (up to 32 per row, so
-    most workgroups publish and one per row and head block merges), 30
-    launches on one workspace without re-initialising it. Every launch must
-    give the same bits (the counters reset themselves, the merge order is
-    fixed whichever chunk arrives last) and the first must match the
-    oracle."""
+def test_many_chunk_merges_repeated_on_one_workspace(H, layout, in_kernel):
+    """The split merge under load: 64-token chunks (up to 32 per row), 30
+    launches on one workspace without re-initialising it, merged by the
+    combine kernel or inside the decode kernel (most workgroups publish and
+    the last per row and head block merges). Every launch must give the same
+    bits (the counters reset themselves, the merge order is fixed whichever
+    chunk arrives last) and the first must match the oracle."""
     import sparse_attention_decode_row_amd as dsa
     rng = np.random.default_rng(31 + layout)
     wl = WL.random_case(rng, rows=6, heads=64, D=512, block_size=64, max_len=3000,
                         width=2048)
-    _announce("many-chunk merges, repeated", layout=layout)
-    plan = H.plan_for(wl, chunk_tokens=64, layout=layout)
+    _announce("many-chunk merges, repeated", layout=layout, in_kernel=in_kernel)
+    plan = H.plan_for(wl, chunk_tokens=64, layout=layout, merge_in_kernel=in_kernel)
+    assert plan.info()["merges_chunks"] == (2 if in_kernel else 1)
     info = plan.info()
     print("plan", info)
     assert info["chunks_per_row"] >= 16
@@ -457,7 +461,7 @@ def test_timed_out_merge_poisons_the_workspace_until_reinit(H):
     wl = WL.random_case(rng, rows=4, heads=64, D=512, block_size=64, max_len=3000,
                         width=2048)
     _announce("timed-out merge, sticky status")
-    plan = H.plan_for(wl, chunk_tokens=512, layout=1)
+    plan = H.plan_for(wl, chunk_tokens=512, layout=1, merge_in_kernel=True)
     info = plan.info()
     R, HB, C = wl.rows, info["head_blocks"], info["chunks_per_row"]
     assert C >= 2 and HB == 2
