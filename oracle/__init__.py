@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_oracle_decode.argtypes = (
             [ctypes.c_int32] * 6 + [ctypes.c_uint64] +
             [ctypes.c_double] * 3 + [ctypes.c_void_p] * 7 + [ctypes.c_int32])
+        L.dsa_oracle_decode_qkv.restype = ctypes.c_int
+        L.dsa_oracle_decode_qkv.argtypes = (
+            [ctypes.c_int32] * 7 + [ctypes.c_uint64] +
+            [ctypes.c_double] * 3 + [ctypes.c_void_p] * 7 + [ctypes.c_int32])
         L.dsa_oracle_max_threads.restype = ctypes.c_int32
         L.dsa_oracle_max_threads.argtypes = []
         L.dsa_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
@@ -141,26 +145,38 @@ def max_threads() -> int:
 def decode(q_bits, k_cache, v_cache, block_tables, seq_lens, sel, *,
            block_size: int, bt_stride: int, cache_stride_bytes: int,
            sm_scale: float, k_scale: float, v_scale: float,
-           num_threads: int = 0) -> np.ndarray:
-    """Full decode. q_bits: [R, H, D] uint16 (bf16 bits); caches: uint8 pools;
-    block_tables: int32 (row stride bt_stride, 0 = shared); seq_lens [R];
-    sel [R, W]. Returns float64 [R, H, D]."""
+           num_threads: int = 0, v_dim: int = 0) -> np.ndarray:
+    """Full decode. q_bits: [R, H, Dqk] uint16 (bf16 bits); caches: uint8
+    pools of Dqk-byte tokens; block_tables: int32 (row stride bt_stride, 0 =
+    shared); seq_lens [R]; sel [R, W]. v_dim (default Dqk): the values and the
+    output are the first v_dim bytes of each token (a token with a tail after
+    its latent). Returns float64 [R, H, v_dim]."""
     q_bits = _c(q_bits, np.uint16)
     R, H, D = q_bits.shape
+    Dv = v_dim or D
     sel = _c(sel, np.int32)
     W = sel.shape[1] if sel.ndim == 2 else 0
     k_cache = _c(k_cache, np.uint8).ravel()
     v_cache = k_cache if v_cache is None else _c(v_cache, np.uint8).ravel()
     bt = _c(block_tables, np.int32).ravel()
     sl = _c(seq_lens, np.int32).ravel()
-    out = np.zeros((R, H, D), dtype=np.float64)
-    rc = lib().dsa_oracle_decode(R, H, D, W, int(block_size), int(bt_stride),
-                                 int(cache_stride_bytes), float(sm_scale),
-                                 float(k_scale), float(v_scale),
-                                 q_bits.ctypes.data, k_cache.ctypes.data,
-                                 v_cache.ctypes.data, bt.ctypes.data,
-                                 sl.ctypes.data, sel.ctypes.data,
-                                 out.ctypes.data, int(num_threads))
+    out = np.zeros((R, H, Dv), dtype=np.float64)
+    if Dv == D:
+        rc = lib().dsa_oracle_decode(R, H, D, W, int(block_size), int(bt_stride),
+                                     int(cache_stride_bytes), float(sm_scale),
+                                     float(k_scale), float(v_scale),
+                                     q_bits.ctypes.data, k_cache.ctypes.data,
+                                     v_cache.ctypes.data, bt.ctypes.data,
+                                     sl.ctypes.data, sel.ctypes.data,
+                                     out.ctypes.data, int(num_threads))
+    else:
+        rc = lib().dsa_oracle_decode_qkv(R, H, D, Dv, W, int(block_size), int(bt_stride),
+                                         int(cache_stride_bytes), float(sm_scale),
+                                         float(k_scale), float(v_scale),
+                                         q_bits.ctypes.data, k_cache.ctypes.data,
+                                         v_cache.ctypes.data, bt.ctypes.data,
+                                         sl.ctypes.data, sel.ctypes.data,
+                                         out.ctypes.data, int(num_threads))
     if rc != 0:
         raise ValueError(f"oracle decode rejected its arguments (rc={rc})")
     return out

@@ -88,22 +88,23 @@ int32_t dsa_oracle_max_threads(void) {
 #endif
 }
 
-/* One (row, head): scores against the dequantised latent rows, softmax,
- * weighted sum of the same rows read as V ([attend] DsaDecodeInputs: K and V
- * are the same latent buffer, dequantised with k_scale and v_scale; the output
- * stays in the kv_lora_rank latent space, which [build] o_absorb consumes). */
-static void decode_one_head(int32_t D, int32_t n, const uint64_t* offs,
+/* One (row, head): scores against the dequantised token rows (all Dqk
+ * bytes), softmax, weighted sum of the first Dv bytes of the same rows read
+ * as V ([attend] DsaDecodeInputs: K and V are the same latent buffer,
+ * dequantised with k_scale and v_scale; the output stays in the latent space,
+ * which [build] o_absorb consumes). NoPE tokens have Dqk == Dv. */
+static void decode_one_head(int32_t Dqk, int32_t Dv, int32_t n, const uint64_t* offs,
                             double sm_scale, double k_scale, double v_scale,
                             const uint16_t* q_head, const uint8_t* k_cache,
                             const uint8_t* v_cache, double* s, double* o) {
-  for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+  for (int32_t d = 0; d < Dv; ++d) o[d] = 0.0;
   if (n == 0) return; /* nothing selected: the output row is zero */
 
   double m = -INFINITY;
   for (int32_t i = 0; i < n; ++i) {
     const uint8_t* krow = k_cache + offs[i];
     double dot = 0.0;
-    for (int32_t d = 0; d < D; ++d)
+    for (int32_t d = 0; d < Dqk; ++d)
       dot += dsa_oracle_bf16(q_head[d]) *
              (k_scale * dsa_oracle_fp8_e4m3fn(krow[d]));
     s[i] = sm_scale * dot;
@@ -116,10 +117,10 @@ static void decode_one_head(int32_t D, int32_t n, const uint64_t* offs,
   }
   for (int32_t i = 0; i < n; ++i) {
     const uint8_t* vrow = v_cache + offs[i];
-    for (int32_t d = 0; d < D; ++d)
+    for (int32_t d = 0; d < Dv; ++d)
       o[d] += s[i] * (v_scale * dsa_oracle_fp8_e4m3fn(vrow[d]));
   }
-  for (int32_t d = 0; d < D; ++d) o[d] /= l;
+  for (int32_t d = 0; d < Dv; ++d) o[d] /= l;
 }
 
 int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
@@ -130,11 +131,25 @@ int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
                       const uint8_t* v_cache, const int32_t* block_tables,
                       const int32_t* seq_lens, const int32_t* sel,
                       double* out, int32_t num_threads) {
-  if (rows < 0 || heads <= 0 || kv_lora_rank <= 0 || width < 0 ||
-      block_size <= 0 || bt_stride < 0)
+  return dsa_oracle_decode_qkv(rows, heads, kv_lora_rank, kv_lora_rank, width,
+                               block_size, bt_stride, cache_stride_bytes,
+                               sm_scale, k_scale, v_scale, q, k_cache, v_cache,
+                               block_tables, seq_lens, sel, out, num_threads);
+}
+
+int dsa_oracle_decode_qkv(int32_t rows, int32_t heads, int32_t qk_dim,
+                          int32_t v_dim, int32_t width, int32_t block_size,
+                          int32_t bt_stride, uint64_t cache_stride_bytes,
+                          double sm_scale, double k_scale, double v_scale,
+                          const uint16_t* q, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const int32_t* block_tables,
+                          const int32_t* seq_lens, const int32_t* sel,
+                          double* out, int32_t num_threads) {
+  if (rows < 0 || heads <= 0 || qk_dim <= 0 || v_dim <= 0 || v_dim > qk_dim ||
+      width < 0 || block_size <= 0 || bt_stride < 0)
     return -1;
   if (rows == 0) return 0;
-  const int32_t D = kv_lora_rank;
+  const int32_t D = qk_dim; /* bytes per cached token, and q's width */
 
   /* Per row: the selected set and each member's byte offset. */
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)rows * (size_t)(width ? width : 1));
@@ -174,10 +189,10 @@ int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
     for (int64_t pr = 0; pr < pairs; ++pr) {
       if (!s) continue;
       int32_t r = (int32_t)(pr / heads), h = (int32_t)(pr % heads);
-      decode_one_head(D, count[r], offs + (size_t)r * width, sm_scale,
+      decode_one_head(D, v_dim, count[r], offs + (size_t)r * width, sm_scale,
                       k_scale, v_scale,
                       q + ((size_t)r * heads + h) * (size_t)D, k_cache,
-                      v_cache, s, out + ((size_t)r * heads + h) * (size_t)D);
+                      v_cache, s, out + ((size_t)r * heads + h) * (size_t)v_dim);
     }
     free(s);
   }

@@ -78,6 +78,28 @@ int dsa_oracle_decode(int32_t rows, int32_t heads, int32_t kv_lora_rank,
                       const int32_t* seq_lens, const int32_t* sel,
                       double* out, int32_t num_threads);
 
+/* The decode for cache tokens that carry a tail after the latent: a token is
+ * qk_dim FP8 bytes, its first v_dim of them the latent. The scores run over
+ * all qk_dim bytes of token t's own row, the values and the output over its
+ * first v_dim ([attend] module doc, "NoPE, and why no common/ kernel would
+ * do", and decode_attention's scale comment: a DeepSeek-V4 token is the
+ * 512-wide latent plus a 64-wide rope tail, 576 in all; the tail arrives
+ * already rotated, and belongs to the token whose row holds it).
+ *   q    [rows, heads, qk_dim] bf16 bits
+ *   out  [rows, heads, v_dim] double
+ * Token t of a row sits at page * cache_stride_bytes + (t mod block_size) *
+ * qk_dim. Otherwise as dsa_oracle_decode, which is this function with
+ * qk_dim == v_dim == kv_lora_rank. Returns 0, or -1 on a bad argument
+ * (including v_dim > qk_dim). */
+int dsa_oracle_decode_qkv(int32_t rows, int32_t heads, int32_t qk_dim,
+                          int32_t v_dim, int32_t width, int32_t block_size,
+                          int32_t bt_stride, uint64_t cache_stride_bytes,
+                          double sm_scale, double k_scale, double v_scale,
+                          const uint16_t* q, const uint8_t* k_cache,
+                          const uint8_t* v_cache, const int32_t* block_tables,
+                          const int32_t* seq_lens, const int32_t* sel,
+                          double* out, int32_t num_threads);
+
 /* Number of threads an OpenMP parallel region of the decode would use. */
 int32_t dsa_oracle_max_threads(void);
 
