@@ -304,15 +304,29 @@ constexpr int kParts = 2;     // scoring waves per head group (32 tokens each)
 // the next tile's K and this tile's V load while the current ones are
 // consumed). Otherwise K and V are the same bytes, in four tile buffers:
 // tile i is scored while tile i-1 is accumulated and tiles i+1, i+2 load.
-template <int D, int kGroups, bool kSplitV>
+// kRope: 0, or the width of a rope tail each cached token carries after its
+// D latent bytes ([attend] module doc, "NoPE, and why no common/ kernel would
+// do": the DeepSeek-V4 token, 512 + 64). The tail is scored with the
+// latent (one more MFMA per 16-token block, hi and lo query terms side by
+// side in its 128-deep k dimension) and staged in its own region of each
+// tile buffer; the values and the output are the latent alone.
+template <int D, int kGroups, bool kSplitV, int kRope = 0>
 __global__ __launch_bounds__(4 * kGroups * kWave, 1)
 void dsa_decode_kernel(DecodeArgs a) {
   constexpr int kQKWaves = kParts * kGroups;
   constexpr int kPVWaves = kQKWaves;
   constexpr int kWaves = kQKWaves + kPVWaves;
   constexpr int kThreads = kWave * kWaves;
-  constexpr int kTileBytes = kTile * D;
-  constexpr int kSmemBytes = kBuffers * kTileBytes;
+  static_assert(kRope == 0 || (kRope == 64 && D == 512 && !kSplitV), "rope tail: 512 + 64, one K/V buffer");
+  constexpr int kRowBytes = D + kRope;              // bytes of a cached token
+  constexpr int kTileBytes = kTile * D;             // latent region of a tile buffer
+  constexpr int kTailBytes = kTile * kRope;         // tail region, after the latent
+  constexpr int kBufBytes = kTileBytes + kTailBytes;
+  constexpr int kSmemBytes = kBuffers * kBufBytes;
+  // rows one workgroup takes (its latent-row table is in LDS; the tail's
+  // region leaves room for 1024)
+  constexpr int kMaxChunk = kRope ? kMaxChunkTokens / 2 : kMaxChunkTokens;
+  constexpr int kTailInstr = kTailBytes / (16 * kWave);  // tail DMAs per tile (one per wave)
   constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
   constexpr int kCB = kDBlocks / kPVWaves;          // column blocks per PV wave (all groups)
@@ -338,7 +352,7 @@ void dsa_decode_kernel(DecodeArgs a) {
                 "K operand offsets must fit the LDS instruction offset field");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunkTokens];
+  __shared__ __attribute__((aligned(16))) uint32_t rows_lds[kMaxChunk];
   // softmax weights of a tile as PV B operands: [tile parity][group][operand half][lane] x 16 bytes
   __shared__ __attribute__((aligned(16))) i32x4 xch_p[2][kGroups][2][kWave];
   __shared__ int xch_e[2][kGroups][4][16];  // their E8M0 exponent bytes, per 16-token block and head
@@ -413,13 +427,20 @@ void dsa_decode_kernel(DecodeArgs a) {
   const bool q_ok = q_head < a.H;
   constexpr bool kShareQ = kKSteps >= 2;
   constexpr int kKOwn = kShareQ ? (kKSteps + kQWaysPerGroup - 1) / kQWaysPerGroup : kKSteps;
-  constexpr int kQxOff = 2 * kTileBytes;
-  static_assert(!kShareQ || kGroups * kKSteps * 4096 <= 2 * kTileBytes, "query exchange area");
+  // With a rope tail the exchange holds one more k-step slot (ks = kKSteps)
+  // for the tail's terms, which the first wave of each group converts
+  // (lanes of groups 0 and 1 hold its 64 values).
+  constexpr int kKX = kKSteps + (kRope ? 1 : 0);   // k-step slots in the exchange
+  constexpr int kQxOff = 2 * kBufBytes;
+  static_assert(!kShareQ || kGroups * kKX * 4096 <= 2 * kBufBytes, "query exchange area");
+  static_assert(kRope == 0 || kRope == 64, "the tail is half a k-step");
+  const bool q_tail = kRope && qsub == 0;  // this wave also converts its group's tail
   auto own_ks = [&](int i) { return kShareQ ? kQWaysPerGroup * i + qsub : i; };
   u32x4 qraw[kKOwn][4];
+  u32x4 qtraw[4];
   static_assert(kKOwn == 1, "one k-step of the query per wave (four 16-byte loads)");
   auto load_q = [&]() {
-    const uint16_t* qrow = a.q + ((size_t)r * a.H + (q_ok ? q_head : 0)) * D;
+    const uint16_t* qrow = a.q + ((size_t)r * a.H + (q_ok ? q_head : 0)) * kRowBytes;
 #pragma unroll
     for (int i = 0; i < kKOwn; ++i) {
       const int ks = min(own_ks(i), kKSteps - 1);
@@ -427,12 +448,16 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) qraw[i][v] = *(const u32x4*)(qrow + d0 + 8 * v);
     }
+    if (q_tail)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) qtraw[v] = *(const u32x4*)(qrow + D + 32 * (g & 1) + 8 * v);
   };
   load_q();
 
-  // the block-table DMA has landed once at most the four query loads issued
-  // after it are outstanding (the window loop's barriers then publish it)
-  wait_vmcnt<4 * kKOwn>();
+  // the block-table DMA has landed once at most the query loads issued after
+  // it are outstanding (the window loop's barriers then publish it)
+  if (q_tail) wait_vmcnt<4 * kKOwn + 4>();
+  else wait_vmcnt<4 * kKOwn>();
 
   uint32_t* bitmap = (uint32_t*)smem;
   const DSA_LDS u32x4* bitmap4 = (const DSA_LDS u32x4*)smem;
@@ -516,7 +541,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           rows_lds[rank - cstart] = lrow;
           if (exporter) {
             a.ws_ids[(size_t)r * a.width + rank] = t;
-            a.ws_offsets[(size_t)r * a.width + rank] = (uint64_t)lrow * (uint64_t)D;
+            a.ws_offsets[(size_t)r * a.width + rank] = (uint64_t)lrow * (uint64_t)kRowBytes;
           }
         }
       }
@@ -561,7 +586,7 @@ void dsa_decode_kernel(DecodeArgs a) {
                      uint32_t c0) {
     const int slot0 = pw_s * kTPW + k * kTokPerInstr;
     const uint32_t chunk = c0 ^ ((uint32_t)tile_swizzle<D>(slot0) << 4);  // < D
-    const uint64_t off = (uint64_t)row * (uint64_t)D | (uint64_t)chunk;
+    const uint64_t off = (uint64_t)row * (uint64_t)kRowBytes + (uint64_t)chunk;
     dma16(src + off, (DSA_LDS void*)(lds + dst_off + slot0 * D));
   };
   auto issue_tile = [&](int tile, int dst_off, const uint8_t* src) {
@@ -576,15 +601,38 @@ void dsa_decode_kernel(DecodeArgs a) {
     return w * kTPW + (sw % kTokPerInstr) * kInstr + sw / kTokPerInstr;
   };
   // LDS byte offsets of the buffers holding tile i's K and V.
-  auto k_off = [&](int i) { return kSplitV ? (i & 1) * kTileBytes : (i & 3) * kTileBytes; };
-  auto v_off = [&](int i) { return kSplitV ? (2 + (i & 1)) * kTileBytes : (i & 3) * kTileBytes; };
+  auto k_off = [&](int i) { return kSplitV ? (i & 1) * kBufBytes : (i & 3) * kBufBytes; };
+  auto v_off = [&](int i) { return kSplitV ? (2 + (i & 1)) * kBufBytes : (i & 3) * kBufBytes; };
+  // Rope tail of a tile: wave w < kTailInstr moves LDS slots 16w .. 16w + 15,
+  // lane l the 16 bytes at position l % 4 of slot 16w + l / 4, which hold the
+  // token the latent region holds at that slot. The tail's 16-byte chunks are
+  // XOR-permuted by bits 2-3 of the slot, so the 16 slots one MFMA operand
+  // read touches land in distinct bank groups.
+  auto tail_dma = [&](int tile, int buf_off) {
+    if (kRope && wave < kTailInstr && tile < ntiles) {
+      const int slot = 16 * wave + (lane >> 2);
+      const uint32_t row = rows_l[tile * kTile + token_of_slot(slot)];
+      const uint32_t chunk = (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)) << 4;
+      dma16(a.k_cache + (uint64_t)row * kRowBytes + D + chunk,
+            (DSA_LDS void*)(lds + buf_off + kTileBytes + wave * 16 * kWave));
+    }
+  };
+  // Tile it has landed for this wave once only the DMAs of the next tile
+  // (issued in the previous step) may still be outstanding.
+  auto wait_tile = [&](int it) {
+    if (kSplitV || it + 1 >= ntiles) wait_vmcnt<0>();
+    else if (kRope && wave < kTailInstr) wait_vmcnt<kInstr + 1>();
+    else wait_vmcnt<kInstr>();
+  };
   // The first tiles (tile 0; with K and V the same bytes also tile 1) go out
   // now; a separate V buffer is filled in the loop after every wave has read
   // its query terms out of it.
   auto issue_first = [&]() {
     if (dma_wave) {
       if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
+      tail_dma(0, k_off(0));
       if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
+      tail_dma(1, k_off(1));
     }
   };
   // ---- the query as two FP8 terms under a per-head power-of-two scale that
@@ -601,6 +649,17 @@ void dsa_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[i][v][e])), fabsf(bf16_hi(qraw[i][v][e]))));
+  }
+  if (q_tail) {
+    // lanes of groups 0 and 1 hold the tail's 64 values; the rest none
+    if (!q_ok || g >= 2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) qtraw[v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qtraw[v][e])), fabsf(bf16_hi(qtraw[v][e]))));
   }
   amax = max_xor32(max_xor16(amax));
   // The first tiles load while the query terms are prepared (issued after
@@ -621,27 +680,40 @@ void dsa_decode_kernel(DecodeArgs a) {
     const float qs = pow2i(sh);
     // exchange area: [group][ks][hi|lo][half][lane]
     u32x4* qx = (u32x4*)(smem + kQxOff);
-#pragma unroll
-    for (int i = 0; i < kKOwn; ++i) {
-      const int ks = own_ks(i);
-      if (ks >= kKSteps) continue;
-      u32x4 h[2], l[2];
+    // 32 bf16 values (16 words) -> hi and lo FP8 terms, 8 words each
+    auto split_q = [&](const u32x4 (&raw)[4], u32x4 (&h)[2], u32x4 (&l)[2]) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const unsigned w0 = qraw[i][v][2 * h2], w1 = qraw[i][v][2 * h2 + 1];
+          const unsigned w0 = raw[v][2 * h2], w1 = raw[v][2 * h2 + 1];
           int hi, lo;
           split_fp8x4(bf16_lo(w0) * qs, bf16_hi(w0) * qs, bf16_lo(w1) * qs, bf16_hi(w1) * qs,
                       hi, lo);
           h[v >> 1][2 * (v & 1) + h2] = (unsigned)hi;
           l[v >> 1][2 * (v & 1) + h2] = (unsigned)lo;
         }
+    };
+    if (q_tail) {
+      u32x4 h[2], l[2];
+      split_q(qtraw, h, l);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        qx[(((hg * kKX + kKSteps) * 2 + 0) * 2 + half) * kWave + lane] = h[half];
+        qx[(((hg * kKX + kKSteps) * 2 + 1) * 2 + half) * kWave + lane] = l[half];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kKOwn; ++i) {
+      const int ks = own_ks(i);
+      if (ks >= kKSteps) continue;
+      u32x4 h[2], l[2];
+      split_q(qraw[i], h, l);
       if constexpr (kShareQ) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + half) * kWave + lane] = h[half];
-          qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + half) * kWave + lane] = l[half];
+          qx[(((hg * kKX + ks) * 2 + 0) * 2 + half) * kWave + lane] = h[half];
+          qx[(((hg * kKX + ks) * 2 + 1) * 2 + half) * kWave + lane] = l[half];
         }
       } else {
         qhi[ks] = i32x8{(int)h[0].x, (int)h[0].y, (int)h[0].z, (int)h[0].w,
@@ -654,17 +726,27 @@ void dsa_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();  // the groups' FP8 terms visible
 
+  // The tail's B operand: k 0..63 its hi terms, k 64..127 its lo terms, so
+  // one MFMA per block adds K_tail . (hi + lo). Lane group G takes the
+  // words that lane group G % 2 converted, hi for G < 2 and lo otherwise.
+  i32x8 qtail = {0, 0, 0, 0, 0, 0, 0, 0};
   if constexpr (kShareQ) {
     if (is_qk) {
       const u32x4* qx = (const u32x4*)(smem + kQxOff);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        const u32x4 h0 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 0) * kWave + lane];
-        const u32x4 h1 = qx[(((hg * kKSteps + ks) * 2 + 0) * 2 + 1) * kWave + lane];
-        const u32x4 l0 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 0) * kWave + lane];
-        const u32x4 l1 = qx[(((hg * kKSteps + ks) * 2 + 1) * 2 + 1) * kWave + lane];
+        const u32x4 h0 = qx[(((hg * kKX + ks) * 2 + 0) * 2 + 0) * kWave + lane];
+        const u32x4 h1 = qx[(((hg * kKX + ks) * 2 + 0) * 2 + 1) * kWave + lane];
+        const u32x4 l0 = qx[(((hg * kKX + ks) * 2 + 1) * 2 + 0) * kWave + lane];
+        const u32x4 l1 = qx[(((hg * kKX + ks) * 2 + 1) * 2 + 1) * kWave + lane];
         qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
         qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      }
+      if constexpr (kRope > 0) {
+        const int src = (g & 1) * 16 + li;
+        const u32x4 t0 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 0) * kWave + src];
+        const u32x4 t1 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 1) * kWave + src];
+        qtail = i32x8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
       }
     }
   }
@@ -779,14 +861,14 @@ void dsa_decode_kernel(DecodeArgs a) {
           // this wave's share of tile it has landed (the next tile's may
           // still be in flight); after the barrier tile it's K is in LDS and
           // every read of the weights of it - 2 is done
-          if (!kSplitV && it + 1 < ntiles) wait_vmcnt<kInstr>();
-          else wait_vmcnt<0>();
+          wait_tile(it);
           barrier_lds();
           const bool score = it < ntiles;
           uint32_t drow[kNd];
           uint32_t c0 = dma_c0;
           asm volatile("" : "+v"(c0));
           if (dma_wave) dma_rows(it, drow);
+          if (!kSplitV) tail_dma(it + 2, k_off(it + 2));
 
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
@@ -808,8 +890,19 @@ void dsa_decode_kernel(DecodeArgs a) {
               }
               return kop;
             };
+            // Rope tail of block k: slot 32*part + 16*k + li, bytes
+            // 32*(g & 1) .. + 31 (chunks XOR-permuted by slot bits 2-3).
+            auto load_tail = [&](int k) -> i32x8 {
+              const DSA_LDS uint8_t* tb = kt + kTileBytes + (32 * part + 16 * k + li) * kRope;
+              const int sw = (li >> 2) & 3, c = 2 * (g & 1);
+              const u32x4 lo = *(const DSA_LDS u32x4*)(tb + 16 * (c ^ sw));
+              const u32x4 hi = *(const DSA_LDS u32x4*)(tb + 16 * ((c + 1) ^ sw));
+              return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            };
             constexpr int kKPre = 3;
             i32x8 kbuf[kKPre + 1];
+            i32x8 ktail = {0, 0, 0, 0, 0, 0, 0, 0};
             // The scoring wave's matrix work goes first on its SIMD; the PV
             // wave's then runs under this wave's softmax.
             __builtin_amdgcn_s_setprio(2);
@@ -819,12 +912,14 @@ void dsa_decode_kernel(DecodeArgs a) {
             for (int s = 0; s < kSteps; ++s) {
               const int k = s / kKSteps, ks = s % kKSteps;
               if (s + kKPre < kSteps) kbuf[(s + kKPre) % (kKPre + 1)] = load_k(s + kKPre);
+              if (kRope && ks == 0) ktail = load_tail(k);
 #pragma unroll
               for (int d = s * kNd / kSteps; d < (s + 1) * kNd / kSteps; ++d) dma_step(it, d, drow, c0);
               __builtin_amdgcn_sched_barrier(0);
               if (ks == 0) S[k] = f32x4{0.f, 0.f, 0.f, 0.f};
               S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qhi[ks], S[k]);
               S[k] = mfma_fp8(kbuf[s % (kKPre + 1)], qlo[ks], S[k]);
+              if (kRope && ks == kKSteps - 1) S[k] = mfma_fp8(ktail, qtail, S[k]);
               __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
@@ -895,8 +990,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           // Tile it has landed: wait for every DMA of this wave but the next
           // tile's, then the barrier (tile it - 1's V and weights visible,
           // every read of tile it - 2's buffer done).
-          if (!kSplitV && it + 1 < ntiles) wait_vmcnt<kInstr>();
-          else wait_vmcnt<0>();
+          wait_tile(it);
           barrier_lds();
           if (pass == 0 && it == 0) barrier_lds();  // the scoring waves' reference exchange
 
@@ -904,6 +998,8 @@ void dsa_decode_kernel(DecodeArgs a) {
           uint32_t c0 = dma_c0;
           asm volatile("" : "+v"(c0));
           if (dma_wave) dma_rows(it, drow);
+          // (with 16-head blocks PV waves also move a quarter of the tail)
+          if (!kSplitV) tail_dma(it + 2, k_off(it + 2));
           if (it == 0) {
 #pragma unroll
             for (int d = 0; d < kNd; ++d) dma_step(it, d, drow, c0);
@@ -1255,12 +1351,17 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 // ------------------------------------------------------------------ launch
 
 template <int D, int kGroups>
-hipError_t launch_g(bool split_v, bool combine, dim3 grid, hipStream_t st, const DecodeArgs& args) {
+hipError_t launch_g(bool split_v, bool rope, bool combine, dim3 grid, hipStream_t st,
+                    const DecodeArgs& args) {
   const dim3 block(4 * kGroups * kWave);
-  if (split_v)
+  if (rope) {
+    if constexpr (D == 512)
+      hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false, 64>), grid, block, 0, st, args);
+  } else if (split_v) {
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
-  else
+  } else {
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false>), grid, block, 0, st, args);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !combine) return e;
   constexpr int kUnits = D * kGroups * 4;  // float4s of one (row, head block)'s partial
@@ -1270,10 +1371,10 @@ hipError_t launch_g(bool split_v, bool combine, dim3 grid, hipStream_t st, const
 }
 
 template <int D>
-hipError_t launch_d(int groups, bool split_v, bool combine, dim3 grid, hipStream_t st,
-                    const DecodeArgs& args) {
-  return groups == 1 ? launch_g<D, 1>(split_v, combine, grid, st, args)
-                     : launch_g<D, 2>(split_v, combine, grid, st, args);
+hipError_t launch_d(int groups, bool split_v, bool rope, bool combine, dim3 grid,
+                    hipStream_t st, const DecodeArgs& args) {
+  return groups == 1 ? launch_g<D, 1>(split_v, rope, combine, grid, st, args)
+                     : launch_g<D, 2>(split_v, rope, combine, grid, st, args);
 }
 
 
@@ -1323,6 +1424,11 @@ int check_launch(dsa_decode_plan_t plan, const void* q, const void* k_cache,
       << ", " << v_scale << ")";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
+  // A rope-tail token is one buffer: the values are its latent bytes.
+  if (plan->p.qk_rope_dim != 0 && k_cache != v_cache)
+    return fail(DSA_DECODE_ERR_INVALID,
+                std::string(who) + ": with a rope tail the values are the latent part of "
+                "the same tokens; v_cache must equal k_cache");
   return DSA_DECODE_OK;
 }
 
@@ -1478,7 +1584,7 @@ int enqueue_decode(dsa_decode_plan_t plan, const void* q, const void* k_cache,
   da.ws_arrivals = (int32_t*)(ws + plan->ws.arrivals);
   da.part_o = plan->chunks > 1 ? (float*)(ws + plan->ws.part_o) : nullptr;
   da.part_ml = plan->chunks > 1 ? (float*)(ws + plan->ws.part_ml) : nullptr;
-  da.stride_rows = (uint32_t)(p.cache_stride_bytes / (uint64_t)p.kv_lora_rank);
+  da.stride_rows = (uint32_t)(p.cache_stride_bytes / token_bytes(p));
   da.rows = p.num_rows;
   da.H = p.num_q_heads;
   da.width = p.sel_width;
@@ -1499,14 +1605,15 @@ int enqueue_decode(dsa_decode_plan_t plan, const void* q, const void* k_cache,
   da.merge_in_kernel = plan->merge_in_kernel ? 1 : 0;
   const int groups = plan->heads_per_block / 16;
   const bool split_v = k_cache != v_cache;
+  const bool rope = p.qk_rope_dim != 0;
   const bool combine = plan->chunks > 1 && !plan->merge_in_kernel;
   const dim3 grid(plan->workgroups);
   hipError_t e;
   switch (p.kv_lora_rank) {
-    case 64: e = launch_d<64>(groups, split_v, combine, grid, stream_h, da); break;
-    case 128: e = launch_d<128>(groups, split_v, combine, grid, stream_h, da); break;
-    case 256: e = launch_d<256>(groups, split_v, combine, grid, stream_h, da); break;
-    default: e = launch_d<512>(groups, split_v, combine, grid, stream_h, da); break;
+    case 64: e = launch_d<64>(groups, split_v, rope, combine, grid, stream_h, da); break;
+    case 128: e = launch_d<128>(groups, split_v, rope, combine, grid, stream_h, da); break;
+    case 256: e = launch_d<256>(groups, split_v, rope, combine, grid, stream_h, da); break;
+    default: e = launch_d<512>(groups, split_v, rope, combine, grid, stream_h, da); break;
   }
   if (e != hipSuccess)
     return fail(DSA_DECODE_ERR_LAUNCH,

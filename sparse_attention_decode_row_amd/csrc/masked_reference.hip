@@ -187,6 +187,9 @@ int dsa_decode_masked_reference(const dsa_decode_params* params, const void* q,
   dsa_decode_params p{};
   int st = validate_params(params, &p);
   if (st != DSA_DECODE_OK) return st;
+  if (p.qk_rope_dim != 0)
+    return fail(DSA_DECODE_ERR_UNSUPPORTED,
+                "dsa_decode_masked_reference: tokens with a rope tail are not supported");
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !sel_indices || !out)
     return fail(DSA_DECODE_ERR_INVALID, "dsa_decode_masked_reference: NULL buffer");
   if (!std::isfinite(k_scale) || !std::isfinite(v_scale))

@@ -70,6 +70,17 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
       << " is not compiled in (supported: 64, 128, 256, 512)";
     return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
   }
+  // The rope-tail token is compiled for one shape only: 512 + 64.
+  if (p->qk_rope_dim != 0 && p->qk_rope_dim != 64) {
+    m << "dsa_decode_plan: qk_rope_dim " << p->qk_rope_dim
+      << " is not compiled in (supported: 0, 64)";
+    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
+  }
+  if (p->qk_rope_dim == 64 && p->kv_lora_rank != 512) {
+    m << "dsa_decode_plan: a 64-wide rope tail is compiled for kv_lora_rank 512 only, got "
+      << p->kv_lora_rank;
+    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
+  }
   if (p->sel_width <= 0) {
     m << "dsa_decode_plan: sel_width must be > 0, got " << p->sel_width;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
@@ -83,22 +94,22 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
       << p->block_table_stride;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  const uint64_t row_bytes =
-      (uint64_t)p->block_size * (uint64_t)p->kv_lora_rank;
+  const uint64_t tok = token_bytes(*p);  // kv_lora_rank (+ qk_rope_dim)
+  const uint64_t row_bytes = (uint64_t)p->block_size * tok;
   const uint64_t stride = p->cache_stride_bytes ? p->cache_stride_bytes : row_bytes;
   if (stride < row_bytes) {
     m << "dsa_decode_plan: cache_stride_bytes " << stride
-      << " is smaller than one page (block_size * kv_lora_rank = " << row_bytes << ")";
+      << " is smaller than one page (block_size * token bytes = " << row_bytes << ")";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  // Latent rows are addressed by index (byte offset / kv_lora_rank), so a
+  // Token rows are addressed by index (byte offset / token bytes), so a
   // page must start on a row boundary.
-  if (stride % (uint64_t)p->kv_lora_rank != 0) {
+  if (stride % tok != 0) {
     m << "dsa_decode_plan: cache_stride_bytes " << stride
-      << " is not a multiple of kv_lora_rank " << p->kv_lora_rank;
+      << " is not a multiple of the token's " << tok << " bytes";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  if (stride / (uint64_t)p->kv_lora_rank > UINT32_MAX) {
+  if (stride / tok > UINT32_MAX) {
     m << "dsa_decode_plan: cache_stride_bytes " << stride
       << " spans more than 2^32 latent rows";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
@@ -119,10 +130,10 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
   }
   if (p->chunk_tokens < 0 ||
       (p->chunk_tokens > 0 && (p->chunk_tokens % kTileTokens != 0 ||
-                               p->chunk_tokens > kMaxChunkTokens))) {
+                               p->chunk_tokens > max_chunk_tokens(*p)))) {
     m << "dsa_decode_plan: chunk_tokens " << p->chunk_tokens
       << " must be 0 or a multiple of " << kTileTokens << " up to "
-      << kMaxChunkTokens;
+      << max_chunk_tokens(*p);
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
   if (p->rows_per_sequence < 0 ||
@@ -137,11 +148,6 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
   if ((p->flags & ~(DSA_DECODE_FLAG_EXPORT_SELECTION | DSA_DECODE_FLAG_MERGE_IN_KERNEL)) != 0) {
     m << "dsa_decode_plan: unknown flags 0x" << std::hex << p->flags;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
-  }
-  if (p->qk_rope_dim != 0) {
-    m << "dsa_decode_plan: qk_rope_dim " << p->qk_rope_dim
-      << " is not compiled in (supported: 0)";
-    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
   }
   if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS16) {
     m << "dsa_decode_plan: layout " << p->layout
@@ -187,7 +193,7 @@ void plan_layout(dsa_decode_plan_s* plan) {
     int64_t per_wg = (wmax * units + wg_target - 1) / wg_target;
     ct = (per_wg + kTileTokens - 1) / kTileTokens * kTileTokens;
     ct = std::max<int64_t>(ct, kTileTokens);
-    ct = std::min<int64_t>(ct, kMaxChunkTokens);
+    ct = std::min<int64_t>(ct, max_chunk_tokens(p));
   }
   const int64_t wmax_tiles = (wmax + kTileTokens - 1) / kTileTokens * kTileTokens;
   ct = std::min<int64_t>(ct, std::max<int64_t>(wmax_tiles, kTileTokens));
@@ -203,7 +209,7 @@ void plan_layout(dsa_decode_plan_s* plan) {
   plan->chunk_lead = 0;
   plan->merge_in_kernel = (p.flags & DSA_DECODE_FLAG_MERGE_IN_KERNEL) != 0;
   if (plan->chunks > 1 && p.chunk_tokens == 0 && plan->merge_in_kernel) {
-    const int64_t lead = std::min<int64_t>(2 * kTileTokens, kMaxChunkTokens - ct);
+    const int64_t lead = std::min<int64_t>(2 * kTileTokens, max_chunk_tokens(p) - ct);
     if (lead > 0 && ct > lead) {
       plan->chunk_lead = (int)lead;
       // The lead can leave the last chunk without any rank: count the chunks

@@ -16,6 +16,16 @@ constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
 // Largest chunk one workgroup handles (its latent-row table lives in LDS:
 // 2048 x 4 B = 8 KiB).
 constexpr int kMaxChunkTokens = 2048;
+// A plan's largest chunk: a workgroup holds its latent-row table in LDS, and
+// with a rope tail the tail's staging area leaves room for half as many.
+inline int max_chunk_tokens(const dsa_decode_params& p) {
+  return p.qk_rope_dim ? kMaxChunkTokens / 2 : kMaxChunkTokens;
+}
+// Bytes of one cached token.
+inline uint64_t token_bytes(const dsa_decode_params& p) {
+  return (uint64_t)p.kv_lora_rank + (uint64_t)p.qk_rope_dim;
+}
+
 // Heads one workgroup covers: 2 groups of 16 heads (four waves per group),
 // or a single group.
 constexpr int kHeadsPerBlock = 32;

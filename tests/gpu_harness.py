@@ -50,7 +50,7 @@ def plan_for(wl: WL.Workload, chunk_tokens: int = 0, max_seq_len=None,
                     chunk_tokens=chunk_tokens, layout=layout,
                     rows_per_sequence=rows_per_sequence,
                     export_selection=export_selection, merge_in_kernel=merge_in_kernel,
-                    device=torch.cuda.current_device())
+                    qk_rope_dim=wl.rope, device=torch.cuda.current_device())
 
 
 def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
@@ -68,7 +68,8 @@ def run_gpu(wl: WL.Workload, *, k_pool=None, v_pool=None, chunk_tokens: int = 0,
     sl = i32(wl.seq_lens if seq_lens is None else seq_lens)
     sl_ = wl.sel if sel is None else sel
     s = i32(sl_)
-    out = torch.full_like(q, float("nan"))
+    out = torch.full((wl.rows, wl.heads, wl.D), float("nan"), dtype=torch.bfloat16,
+                     device=dev())
     plan = plan_for(wl, chunk_tokens, max_seq_len=max_seq_len, layout=layout,
                     rows_per_sequence=rows_per_sequence, export_selection=with_selection,
                     merge_in_kernel=merge_in_kernel)
@@ -107,7 +108,7 @@ def oracle_rows(wl: WL.Workload, rows, *, host_pool=None, host_v_pool=None,
                          block_size=wl.block_size, bt_stride=wl.bt_stride,
                          cache_stride_bytes=wl.cache_stride_bytes,
                          sm_scale=wl.sm_scale, k_scale=wl.k_scale,
-                         v_scale=wl.v_scale)
+                         v_scale=wl.v_scale, v_dim=wl.D)
 
 
 def normwise_err(got: np.ndarray, want: np.ndarray) -> np.ndarray:
@@ -133,7 +134,7 @@ def check_selection(wl: WL.Workload, run: GpuRun, rows=None, sel=None, seq_lens=
         if check_offsets:
             table = wl.block_tables[r if wl.bt_stride else 0]
             want_off = np.array([oracle.token_offset(table, int(t), wl.block_size,
-                                                     wl.cache_stride_bytes, wl.D)
+                                                     wl.cache_stride_bytes, wl.token_bytes)
                                  for t in want], dtype=np.uint64)
             assert np.array_equal(run.offsets[r, :n], want_off), f"row {r}: offsets differ"
 

@@ -63,8 +63,15 @@ def plan(native, **kw):
     (dict(max_seq_len=0), -1, "max_seq_len must be > 0"),
     (dict(block_table_stride=-1), -1, "block_table_stride must be >= 0"),
     (dict(cache_stride_bytes=1000), -1, "smaller than one page"),
-    (dict(cache_stride_bytes=64 * 512 + 8), -1, "not a multiple of kv_lora_rank"),
-    (dict(cache_stride_bytes=64 * 512 + 256), -1, "not a multiple of kv_lora_rank"),
+    (dict(cache_stride_bytes=64 * 512 + 8), -1, "not a multiple of the token's 512 bytes"),
+    (dict(cache_stride_bytes=64 * 512 + 256), -1, "not a multiple of the token's 512 bytes"),
+    (dict(qk_rope_dim=32), -2, "qk_rope_dim 32 is not compiled in"),
+    (dict(qk_rope_dim=64, kv_lora_rank=256), -2, "kv_lora_rank 512 only"),
+    (dict(qk_rope_dim=64, cache_stride_bytes=64 * 512), -1, "smaller than one page"),
+    (dict(qk_rope_dim=64, cache_stride_bytes=64 * 576 + 512), -1,
+     "not a multiple of the token's 576 bytes"),
+    (dict(qk_rope_dim=64, chunk_tokens=2048), -1, "up to 1024"),
+    (dict(flags=8), -1, "unknown flags"),
     (dict(block_table_stride=100), -1, "block-table entries per row"),
     (dict(sm_scale=float("inf")), -1, "sm_scale must be finite"),
     (dict(chunk_tokens=100), -1, "chunk_tokens"),
@@ -93,6 +100,30 @@ def test_no_gpu_means_device_error(native):
     with pytest.raises(native.DsaDecodeError) as e:
         native.Plan(device=0, **GOOD)
     assert e.value.status == native.DSA_DECODE_ERR_DEVICE
+
+
+def test_rope_tail_plans(native):
+    # 576-byte tokens: pages of block_size such tokens by default, at most
+    # 1024 tokens per workgroup, so a 2048-wide row is split in two
+    p = plan(native, qk_rope_dim=64).info()
+    assert p["qk_rope_dim"] == 64
+    assert p["chunk_tokens"] == 1024 and p["chunks_per_row"] == 2
+    assert p["merges_chunks"] == 1
+    q = plan(native, qk_rope_dim=64, cache_stride_bytes=64 * 576 * 2).info()
+    assert q["chunks_per_row"] == 2
+    # the in-kernel merge's lead must still leave chunk 0 within 1024 tokens
+    m = plan(native, qk_rope_dim=64, num_rows=32, max_seq_len=8192, block_table_stride=128,
+             merge_in_kernel=True).info()
+    assert m["chunk_tokens"] + m["chunk_lead"] <= 1024
+
+
+def test_masked_reference_refuses_rope_tail(native):
+    P = native.Params(2, 4, 1, 512, 64, 4, 32, 16, 0, 1000, 0.1, 0, 0, 0, 0, 64,
+                      (ctypes.c_int32 * 2)(0, 0))
+    rc = native.lib().dsa_decode_masked_reference(ctypes.byref(P), 1, 1, 1, 1, 1, 1,
+                                                  0.05, 0.05, 1, None)
+    assert rc == native.DSA_DECODE_ERR_UNSUPPORTED
+    assert "rope" in native.last_error()
 
 
 def test_shared_table_skips_capacity_rule(native):

@@ -67,11 +67,16 @@ class Workload:
     block_tables: np.ndarray    # [R, bt_stride] int32
     seq_lens: np.ndarray        # [R] int32
     sel: np.ndarray             # [R, W] int32
-    pool: Optional[np.ndarray] = None  # [num_pages * block_size * D] uint8, host pools only
+    pool: Optional[np.ndarray] = None  # [num_pages * block_size * token_bytes] uint8, host pools only
+    rope: int = 0               # rope-tail bytes each token carries after its D latent bytes
 
     @property
     def pool_bytes(self) -> int:
         return self.num_pages * self.cache_stride_bytes
+
+    @property
+    def token_bytes(self) -> int:
+        return self.D + self.rope
 
 
 # ----------------------------------------------------------------- primitives
@@ -262,6 +267,25 @@ def make(name: str, *, sel_seed: int = 0, with_pool: bool = True) -> Workload:
         wl.pool = host_pool(np.random.default_rng([seed, 7]), num_pages, B, D,
                             sigma, ks)
     return wl
+
+
+def with_rope_tail(wl: Workload, rope: int = 64, seed: int = 5) -> Workload:
+    """The same workload with tokens that carry a rope tail after the latent
+    (the DeepSeek-V4 token of [attend]'s module doc: 512 + 64 bytes): q gains
+    `rope` values per head (N(0,1), bf16), the pool is redrawn with the same
+    recipe at D + rope bytes per token, pages of block_size such tokens, and
+    the softmax scale becomes 1/sqrt(D + rope). Tables and selections are
+    unchanged."""
+    rng = np.random.default_rng([wl.seed if wl.seed >= 0 else 0, seed])
+    R, H = wl.rows, wl.heads
+    tail = bf16_bits_from_f32(rng.standard_normal((R, H, rope), dtype=np.float32))
+    q_bits = np.concatenate([wl.q_bits, tail], axis=2)
+    tb = wl.D + rope
+    pool = host_pool(rng, wl.num_pages, wl.block_size, tb, wl.sigma, wl.k_scale)
+    return dataclasses.replace(
+        wl, name=wl.name + f"+rope{rope}", q_bits=np.ascontiguousarray(q_bits),
+        cache_stride_bytes=wl.block_size * tb, sm_scale=1.0 / math.sqrt(tb), pool=pool,
+        rope=rope)
 
 
 def pages_of_rows(wl: Workload, rows) -> np.ndarray:
