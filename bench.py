@@ -51,7 +51,15 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB "
                          "(reference dispatch for HBM counter calibration)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="cold runs: write this many MiB (>= 512 evicts the 256 MiB "
+                         "last-level cache) before every timed decode launch and time each "
+                         "launch with its own event pair (reported as 'cold'; a kernel trace "
+                         "gives the exact durations)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--rope-tail", action="store_true",
+                    help="576-byte tokens: the latent plus a 64-byte rope tail (q 576 wide, "
+                         "scores over 576, values over 512); no CPU baseline")
     ap.add_argument("--merge-in-kernel", action="store_true",
                     help="split rows merged by their last chunk inside the decode "
                          "kernel instead of by the combine kernel")
@@ -88,33 +96,49 @@ def main():
 
     base = WL.make(name, with_pool=False)
     R, H, D, W = base.rows, base.heads, base.D, base.width
-    pool = WL.device_pool(base.num_pages, base.block_size, D, base.sigma,
+    rope = 64 if args.rope_tail else 0
+    TB = D + rope                                     # bytes per cached token
+    if rope:
+        import dataclasses
+        import math
+        base = dataclasses.replace(base, rope=rope, cache_stride_bytes=base.block_size * TB,
+                                   sm_scale=1.0 / math.sqrt(TB))
+        args.cpu_rows = 0
+    pool = WL.device_pool(base.num_pages, base.block_size, TB, base.sigma,
                           base.k_scale, seed=base.seed)
     bt = torch.from_numpy(base.block_tables).to(dev)
     sl = torch.from_numpy(base.seq_lens).to(dev)
     batches = []
     uniq_per_step = []
+    union_per_step = []
+    rows_per_seq = (args.rows_per_sequence if args.rows_per_sequence >= 0
+                    else (4 if name == "verify" else 1))
     for s in range(args.sets):
         wl = base if s == 0 else WL.make(name, sel_seed=s, with_pool=False)
-        qb = np.random.default_rng([base.seed, 100 + s]).standard_normal((R, H, D), dtype=np.float32)
+        qb = np.random.default_rng([base.seed, 100 + s]).standard_normal((R, H, TB), dtype=np.float32)
         q = torch.from_numpy(WL.bf16_bits_from_f32(qb).view(np.int16)).to(dev).view(torch.bfloat16)
         sel = torch.from_numpy(wl.sel).to(dev)
         batches.append((q, sel))
         n = 0
+        sets = []
         for r in range(R):
             row = wl.sel[r]
-            n += int(np.unique(row[(row >= 0) & (row < wl.seq_lens[r])]).size)
+            sets.append(np.unique(row[(row >= 0) & (row < wl.seq_lens[r])]))
+            n += int(sets[-1].size)
         uniq_per_step.append(n)
+        # decode_k rows of one sequence: the union of their selections is what
+        # the sequence needs from memory once
+        k = max(rows_per_seq, 1)
+        union_per_step.append(sum(int(np.unique(np.concatenate(sets[i:i + k])).size)
+                                  for i in range(0, R, k)))
     out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
     # the verify workload holds 4 consecutive decode_k rows per sequence
-    rows_per_seq = (args.rows_per_sequence if args.rows_per_sequence >= 0
-                    else (4 if name == "verify" else 1))
     plan = dsa.Plan(num_rows=R, num_q_heads=H, kv_lora_rank=D,
                     block_size=base.block_size, index_kpool=base.kpool, sel_width=W,
                     block_table_stride=base.bt_stride, max_seq_len=base.max_seq_len,
                     sm_scale=base.sm_scale, cache_stride_bytes=base.cache_stride_bytes,
                     chunk_tokens=args.chunk_tokens, merge_in_kernel=args.merge_in_kernel,
-                    rows_per_sequence=rows_per_seq, device=0)
+                    qk_rope_dim=rope, rows_per_sequence=rows_per_seq, device=0)
     ws = plan.new_workspace(0)
     info = plan.info()
     stream = torch.cuda.current_stream()
@@ -158,8 +182,8 @@ def main():
     tokens = float(np.mean([uniq_per_step[(args.warmup + i) % args.sets] for i in range(K)]))
     value = tokens / (ms_per_step / 1e3)
     kern_ms = event_ms / K
-    gathered_bytes = tokens * D                      # FP8 latent bytes per launch
-    flops = 4.0 * H * D * tokens                     # QK^T + PV
+    gathered_bytes = tokens * TB                     # FP8 token bytes per launch
+    flops = 2.0 * H * (TB + D) * tokens              # QK^T over TB + PV over D
     achieved_gbps = gathered_bytes / (kern_ms / 1e3) / 1e9
     tflops = flops / (kern_ms / 1e3) / 1e12
 
@@ -177,7 +201,9 @@ def main():
         "dtype": "fp8",
         "data": "synthetic",
         "config": {
-            "workload": f"{name}: {R} rows x {H} heads, kv_lora_rank {D}, {W} selected ids "
+            "workload": f"{name}: {R} rows x {H} heads, kv_lora_rank {D}"
+                        + (f" + {rope}-byte rope tail" if rope else "")
+                        + f", {W} selected ids "
                         f"per row of a {int(base.max_seq_len)}-token context, block_size "
                         f"{base.block_size}, FP8 E4M3 pool {base.pool_bytes / 2**30:.1f} GiB",
             "rows": R, "heads": H, "kv_lora_rank": D, "sel_width": W,
@@ -209,7 +235,18 @@ def main():
                  "fp8_issued_flops_per_launch": 2 * flops, "fp8_peak": 5000.0},
     }
 
-    measured = measured_traffic(name, rows_per_sequence=rows_per_seq)
+    if rows_per_seq > 1:
+        utok = float(np.mean([union_per_step[(args.warmup + i) % args.sets] for i in range(K)]))
+        ub = utok * TB
+        result["union"] = {
+            "rows_per_sequence": rows_per_seq, "tokens_per_step": utok, "gathered_bytes": ub,
+            "achieved": ub / (kern_ms / 1e3) / 1e9, "unit": "GB/s",
+            "frac": ub / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "note": "the distinct tokens each sequence's rows select, fetched once per "
+                    "sequence: the bytes the method needs from memory"}
+    if args.flush_mib:
+        result["cold"] = cold_run(args, step, stream, D, TB, H, uniq_per_step)
+    measured = None if rope else measured_traffic(name, rows_per_sequence=rows_per_seq)
     if measured is not None:
         result["roofline"]["traffic"] = measured
         result["roofline"]["traffic_unit"] = ("bytes per launch, rocprofv3 FETCH_SIZE + WRITE_SIZE "
@@ -217,6 +254,33 @@ def main():
     if args.cpu_rows > 0:
         result["cpu_baseline"] = cpu_baseline(base, pool, batches[0], args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def cold_run(args, step, stream, D, TB, H, uniq_per_step):
+    """Decode launches with the caches flushed before each: a write of
+    args.flush_mib MiB, then the launch between its own event pair."""
+    import numpy as np
+    import torch
+    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=stream.device)
+    n = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        flush.fill_(i & 0xFF)
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    tokens = float(np.mean([uniq_per_step[i % args.sets] for i in range(n)]))
+    med = float(np.median(us))
+    return {"flush_mib": args.flush_mib, "launches": n, "kernel_us_median_events": med,
+            "kernel_us_mean_events": float(us.mean()),
+            "roofline_frac": tokens * TB / (med / 1e6) / 1e9 / HBM_PEAK_GBPS,
+            "note": "each launch timed by its own event pair after a cache-flushing "
+                    "write; an event pair adds a few microseconds, so a kernel trace's "
+                    "durations are the precise cold figure"}
 
 
 def calibration_copy(mib):
