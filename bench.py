@@ -52,10 +52,14 @@ def parse():
                     help="also run one plain device copy of this many MiB "
                          "(reference dispatch for HBM counter calibration)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="cold runs: write this many MiB (>= 512 evicts the 256 MiB "
+                    help="cold runs: sweep this many MiB (>= 512 evicts the 256 MiB "
                          "last-level cache) before every timed decode launch and time each "
                          "launch with its own event pair (reported as 'cold'; a kernel trace "
                          "gives the exact durations)")
+    ap.add_argument("--flush-kind", choices=["read", "write"], default="read",
+                    help="cold runs: the sweep reads the buffer (the caches hold clean lines "
+                         "afterwards) or writes it (they hold dirty lines, which the decode's "
+                         "own reads then push out to HBM)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
     ap.add_argument("--rope-tail", action="store_true",
                     help="576-byte tokens: the latent plus a 64-byte rope tail (q 576 wide, "
@@ -257,17 +261,22 @@ def main():
 
 
 def cold_run(args, step, stream, D, TB, H, uniq_per_step):
-    """Decode launches with the caches flushed before each: a write of
-    args.flush_mib MiB, then the launch between its own event pair."""
+    """Decode launches with the caches flushed before each: a sweep over
+    args.flush_mib MiB (a reduction that reads it, or a fill that writes it),
+    then the launch between its own event pair."""
     import numpy as np
     import torch
-    flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=stream.device)
+    flush = torch.ones(args.flush_mib << 17, dtype=torch.int64, device=stream.device)
+    sink = torch.zeros(1, dtype=torch.int64, device=stream.device)
     n = min(args.steps, 200)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n)]
     torch.cuda.synchronize()
     for i in range(n):
-        flush.fill_(i & 0xFF)
+        if args.flush_kind == "read":
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+        else:
+            flush.fill_(i)
         evs[i][0].record(stream)
         step(i)
         evs[i][1].record(stream)
@@ -275,11 +284,11 @@ def cold_run(args, step, stream, D, TB, H, uniq_per_step):
     us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     tokens = float(np.mean([uniq_per_step[i % args.sets] for i in range(n)]))
     med = float(np.median(us))
-    return {"flush_mib": args.flush_mib, "launches": n, "kernel_us_median_events": med,
-            "kernel_us_mean_events": float(us.mean()),
+    return {"flush_mib": args.flush_mib, "flush_kind": args.flush_kind, "launches": n,
+            "kernel_us_median_events": med, "kernel_us_mean_events": float(us.mean()),
             "roofline_frac": tokens * TB / (med / 1e6) / 1e9 / HBM_PEAK_GBPS,
             "note": "each launch timed by its own event pair after a cache-flushing "
-                    "write; an event pair adds a few microseconds, so a kernel trace's "
+                    "sweep; an event pair adds a few microseconds, so a kernel trace's "
                     "durations are the precise cold figure"}
 
 

@@ -1294,6 +1294,11 @@ __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 // (row, head block) reads element group t of each chunk's partial: in the
 // register order that is PV wave src, head group x, column block j, lane
 // (head li, column quarter g), the layout the decode kernel stores.
+// The chunks are read kBatch at a time, every load of a batch issued before
+// any is used (one memory round trip per batch); a later batch with a larger
+// reference rescales the sums so far (with at most kBatch chunks, M is the
+// batch's maximum and nothing is rescaled). The status word was written, if
+// at all, by an earlier kernel on the stream, so a plain load sees it.
 template <int D, int kGroups>
 __global__ __launch_bounds__(256)
 void dsa_combine_kernel(DecodeArgs a) {
@@ -1301,10 +1306,12 @@ void dsa_combine_kernel(DecodeArgs a) {
   constexpr int kCB = D / 16 / kPVWaves;
   constexpr int kUnits = kPVWaves * kGroups * kCB * kWave;  // float4s per chunk partial
   constexpr int kBlocksPerUnit = kUnits / 256;
+  constexpr int kBatch = 4;
   static_assert(kUnits % 256 == 0, "whole blocks per (row, head block)");
   const int rh = blockIdx.x / kBlocksPerUnit;  // r * head_blocks + hb
   const int t = (blockIdx.x % kBlocksPerUnit) * 256 + threadIdx.x;
   if (rh >= a.rows * a.head_blocks) return;
+  const bool bad = *a.ws_status != 0;
   const int r = rh / a.head_blocks, hb = rh % a.head_blocks;
   const int lane = t % kWave, li = lane & 15, g = lane >> 4;
   const int j = (t / kWave) % kCB, x = (t / (kWave * kCB)) % kGroups;
@@ -1312,12 +1319,9 @@ void dsa_combine_kernel(DecodeArgs a) {
   const int hx = hb * a.heads_per_block + x * 16 + li;
   if (hx >= a.H) return;
   const size_t slot0 = (size_t)rh * a.chunks;
-  const float* ml = a.part_ml + (slot0 * a.heads_per_block + x * 16 + li) * 2;
-  const size_t ml_stride = (size_t)a.heads_per_block * 2;
-  float M = -INFINITY;
-  for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, ml[c * ml_stride]);
-  float L = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  // (m_c, l_c) of this head: float pairs, heads_per_block pairs per chunk
+  const float2* ml = (const float2*)a.part_ml + slot0 * a.heads_per_block + x * 16 + li;
+  const size_t ml_stride = (size_t)a.heads_per_block;
   // Each chunk keeps an fp32-sized slot of kUnits * 4 floats, one
   // kPartFloats region per PV wave; the fp16 partial fills the first half
   // of its wave's region, 4 halves per (group, block, lane) unit u.
@@ -1325,15 +1329,37 @@ void dsa_combine_kernel(DecodeArgs a) {
   const int u = t % (kGroups * kCB * kWave);
   const _Float16* p0 = (const _Float16*)(a.part_o + slot0 * kUnits * 4 + src * kPartFloats) + u * 4;
   constexpr size_t kChunkHalves = (size_t)kUnits * 4 * 2;
-#pragma unroll 4
-  for (int c = 0; c < a.chunks; ++c) {
-    const float m = ml[c * ml_stride];
-    const float w = m == -INFINITY ? 0.f : fast_exp2(m - M) * ml[c * ml_stride + 1];
-    L += w;
-    const f16x4 h = *(const f16x4*)(p0 + c * kChunkHalves);
-    o += f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * w;
+  float M = -INFINITY, L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < a.chunks; c0 += kBatch) {
+    float2 mlv[kBatch];
+    f16x4 h[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = min(c0 + k, a.chunks - 1);  // past the last chunk: a repeat, weighted 0
+      mlv[k] = ml[c * ml_stride];
+      h[k] = *(const f16x4*)(p0 + c * kChunkHalves);
+    }
+    float mb = M;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k)
+      if (c0 + k < a.chunks) mb = fmaxf(mb, mlv[k].x);
+    if (mb != M) {  // M < mb: rescale what the earlier batches added (nothing when M is -inf)
+      const float sc = M == -INFINITY ? 0.f : fast_exp2(M - mb);
+      L *= sc;
+      o *= sc;
+      M = mb;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const bool use = c0 + k < a.chunks && mlv[k].x != -INFINITY;  // an empty chunk adds nothing
+      const float w = use ? fast_exp2(mlv[k].x - M) * mlv[k].y : 0.f;
+      const f32x4 hv = use ? f32x4{(float)h[k][0], (float)h[k][1], (float)h[k][2], (float)h[k][3]}
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+      L += w;
+      o += hv * w;
+    }
   }
-  const bool bad = __hip_atomic_load(a.ws_status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
   const float inv = bad ? __builtin_nanf("") : (L > 0.f ? a.v_scale / L : 0.f);
   const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
                     (__bf16)(o[3] * inv)};
