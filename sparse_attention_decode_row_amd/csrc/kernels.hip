@@ -473,6 +473,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // placement below, when the read-back hook is wanted.
   const bool exporter = hb == 0 && a.export_sel;
   const DSA_LDS int32_t* btl = (const DSA_LDS int32_t*)(lds + kSmemBytes / 2);
+  const bool bt_fast = nbt == a.bt_entries && a.bs_shift >= 0 && !exporter;
   int total = 0;
   for (int base = 0; base < L; base += kWinWords * 32) {
     const int span = min(kWinWords * 32, L - base);
@@ -546,8 +547,26 @@ void dsa_decode_kernel(DecodeArgs a) {
         }
       }
     };
+    if (bt_fast) {
+      // The whole block-table row is in LDS, the block size a power of two
+      // and nothing is exported: the preloaded ids branch-free, every lane
+      // reading (a lane outside the window reads word 0 and entry 0 and
+      // stores nothing).
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) place(tpre[u]);
+      for (int u = 0; u < kPre; ++u) {
+        const int t = tpre[u];
+        const unsigned o = (unsigned)t - (unsigned)base;
+        const bool in = o < (unsigned)span;
+        const int w = in ? (int)(o >> 5) : 0;
+        const int rank = total + (int)wrank_l[w] + __popc(bitmap_l[w] & ((1u << (o & 31)) - 1u));
+        const int pi = in ? t >> a.bs_shift : 0;
+        const uint32_t lrow = (uint32_t)btl[pi] * a.stride_rows + (uint32_t)(t & (a.block_size - 1));
+        if (in && rank >= cstart && rank < cend) rows_lds[rank - cstart] = lrow;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) place(tpre[u]);
+    }
     for (int j = tid + kPre * kThreads; j < a.width; j += kThreads) place(srow[j]);
     total += all;
     __syncthreads();  // the id table is complete; the bitmap is reused by the next window
