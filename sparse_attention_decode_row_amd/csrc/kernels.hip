@@ -580,7 +580,37 @@ void dsa_decode_kernel(DecodeArgs a) {
   if (n > 0)
     for (int p = n + tid; p < ntiles * kTile; p += kThreads) rows_lds[p] = rows_lds[n - 1];
 
-  __syncthreads();  // the row table is complete (padded to whole tiles)
+  // ---- the query as two FP8 terms under a per-head power-of-two scale that
+  // puts the head's largest |q| in [128, 256). Each wave's share of the
+  // maximum goes out with the row table (the barrier below publishes both).
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kKOwn; ++i) {
+    const int ks = own_ks(i);
+    if (!q_ok || ks >= kKSteps || 128 * ks + 32 * g >= D)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) qraw[i][v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[i][v][e])), fabsf(bf16_hi(qraw[i][v][e]))));
+  }
+  if (q_tail) {
+    // lanes of groups 0 and 1 hold the tail's 64 values; the rest none
+    if (!q_ok || g >= 2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) qtraw[v] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qtraw[v][e])), fabsf(bf16_hi(qtraw[v][e]))));
+  }
+  amax = max_xor32(max_xor16(amax));
+  if constexpr (kShareQ) xch_f[wave][lane] = amax;
+
+  __syncthreads();  // the row table is complete (padded to whole tiles), the query maxima visible
 
   // -------------------------------------------------------------- 2. gather
   // Wave w (< kDmaWaves) moves tokens [w*kTPW, (w+1)*kTPW) of a tile. Its
@@ -654,39 +684,11 @@ void dsa_decode_kernel(DecodeArgs a) {
       tail_dma(1, k_off(1));
     }
   };
-  // ---- the query as two FP8 terms under a per-head power-of-two scale that
-  // puts the head's largest |q| in [128, 256)
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < kKOwn; ++i) {
-    const int ks = own_ks(i);
-    if (!q_ok || ks >= kKSteps || 128 * ks + 32 * g >= D)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) qraw[i][v] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[i][v][e])), fabsf(bf16_hi(qraw[i][v][e]))));
-  }
-  if (q_tail) {
-    // lanes of groups 0 and 1 hold the tail's 64 values; the rest none
-    if (!q_ok || g >= 2)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) qtraw[v] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qtraw[v][e])), fabsf(bf16_hi(qtraw[v][e]))));
-  }
-  amax = max_xor32(max_xor16(amax));
+
   // The first tiles load while the query terms are prepared (issued after
   // the query registers were first read, so that no wait for the query
   // loads can also wait for these).
   issue_first();
-  if constexpr (kShareQ) xch_f[wave][lane] = amax;
-  __syncthreads();  // the groups' maxima visible
   float score_scale;
   i32x8 qhi[kKSteps], qlo[kKSteps];
   {
