@@ -953,11 +953,23 @@ void dsa_decode_kernel(DecodeArgs a) {
                 for (int i = 0; i < 4; ++i)
                   if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
             }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-              const float m4 = max2(max2(S[k][0], S[k][1], pinf), max2(S[k][2], S[k][3], pinf), pinf);
-              mh[k] = max_xor32(max_xor16(m4, pinf), pinf) * score_scale;  // score_scale > 0
-              m_seen = max2(m_seen, mh[k], pinf);
+            {
+              // Both blocks' maxima over the four lane groups at once. A row
+              // swap of block 0's and block 1's lane maxima leaves rows
+              // (b0 r0, b1 r0, b0 r2, b1 r2) against (b0 r1, b1 r1, b0 r3, b1 r3);
+              // their max, folded across the halves, holds block 0's maximum
+              // in rows 0 and 2 and block 1's in rows 1 and 3, and one more
+              // row swap hands every lane both.
+              const float a0 = max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf);
+              const float a1 = max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf);
+              const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1),
+                                                               false, false);
+              const float d = max_xor32(max2(__uint_as_float(r1[0]), __uint_as_float(r1[1]), pinf), pinf);
+              const auto r3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d),
+                                                               false, false);
+              mh[0] = __uint_as_float(r3[0]) * score_scale;  // score_scale > 0
+              mh[1] = __uint_as_float(r3[1]) * score_scale;
+              m_seen = max2(m_seen, max2(mh[0], mh[1], pinf), pinf);
             }
           }
           if (pass == 0 && it == 0) {
