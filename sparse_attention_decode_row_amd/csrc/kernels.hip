@@ -1116,9 +1116,32 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   };
   if (a.chunks == 1) {
+    // The block's output rows are contiguous in `out`: they are staged in
+    // the (now idle) tile buffers as bf16, rows 2*D + 16 bytes apart so that
+    // the 16 rows one staging store touches fall in distinct banks, and then
+    // written as whole 16-byte pieces, consecutive lanes on consecutive bytes.
+    constexpr int kStageRow = 2 * D + 16;
+    static_assert(kGroups * 16 * kStageRow <= kSmemBytes, "output staging");
     if (!is_qk)
 #pragma unroll
-      for (int x = 0; x < kGroups; ++x) store_out(x, O[x], l_run[x]);
+      for (int x = 0; x < kGroups; ++x) {
+        const float inv = sticky_bad ? __builtin_nanf("") : (l_run[x] > 0.f ? a.v_scale / l_run[x] : 0.f);
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) {
+          const bf16x4 v = {(__bf16)(O[x][j][0] * inv), (__bf16)(O[x][j][1] * inv),
+                            (__bf16)(O[x][j][2] * inv), (__bf16)(O[x][j][3] * inv)};
+          *(bf16x4*)(smem + (x * 16 + li) * kStageRow + 2 * (16 * (jbase + j) + 4 * g)) = v;
+        }
+      }
+    __syncthreads();
+    const int h0 = hb * a.heads_per_block;
+    const int rows = min(a.heads_per_block, a.H - h0);
+    uint8_t* ob = (uint8_t*)(a.out + ((size_t)r * a.H + h0) * D);
+    constexpr int kPieces = 2 * D / 16;  // 16-byte pieces per row
+    for (int i = tid; i < rows * kPieces; i += kThreads) {
+      const int row = i / kPieces, pc = i - row * kPieces;
+      *(u32x4*)(ob + (size_t)row * (2 * D) + 16 * pc) = *(const u32x4*)(smem + row * kStageRow + 16 * pc);
+    }
     return;
   }
   // Split chunks. Each workgroup counts itself in; the last one to arrive
