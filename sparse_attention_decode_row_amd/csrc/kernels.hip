@@ -989,10 +989,11 @@ void dsa_decode_kernel(DecodeArgs a) {
             // ---- weights, per 16-token block: the block's largest weight of
             // the head maps to [128, 256) (a block with no valid token:
             // exponent -100, weights 0)
+            // (an exponent reaches kSlack exactly when the larger block maximum does)
+            overflow |= fmaxf(mh[0], mh[1]) - (mb7 + 7.f) >= kSlack;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
               const float ef = floorf(__builtin_amdgcn_fmed3f(mh[k] - (mb7 + 7.f), -100.f, 100.f));
-              overflow |= ef >= kSlack;
               const float bsub = mb7 + ef;
               const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
               float p[4];
@@ -1006,7 +1007,7 @@ void dsa_decode_kernel(DecodeArgs a) {
               int* dst = (int*)&xch_p[it & 1][hg][part][(2 * k + (g >> 1)) * 16 + li];
               dst[g & 1] = phi;
               dst[2 + (g & 1)] = plo;
-              if (g == 0) xch_e[it & 1][hg][2 * part + k][li] = eb;
+              xch_e[it & 1][hg][2 * part + k][li] = eb;  // (every lane group: the same byte)
             }
           }
         }
