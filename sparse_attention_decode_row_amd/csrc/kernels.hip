@@ -848,12 +848,12 @@ void dsa_decode_kernel(DecodeArgs a) {
   float l_part = 0.f;        // this scoring wave's share of sum_t 2^(s_t - m_ref), per head
   float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
   float mb7 = -7.f;          // (m_ref, or 0 while it is -inf) - 7
-  float m_seen = -INFINITY;  // exact max of this wave's scores so far
+  float m_seen = -INFINITY;  // exact max of this wave's scores so far (unscaled MFMA units)
   // After the first pass: recompute the chunk only if some scoring wave saw
   // a score beyond the slack (every wave takes part; two barriers).
   auto redo_needed = [&](bool overflow) {
     if (__any(overflow) && lane == 0) flag_sh = 1;
-    xch_f[wave][lane] = m_seen;
+    xch_f[wave][lane] = m_seen * score_scale;  // score_scale > 0
     __syncthreads();
     const bool redo = flag_sh != 0;
     if (redo && is_qk) {
@@ -967,15 +967,17 @@ void dsa_decode_kernel(DecodeArgs a) {
               const float d = max_xor32(max2(__uint_as_float(r1[0]), __uint_as_float(r1[1]), pinf), pinf);
               const auto r3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d),
                                                                false, false);
-              mh[0] = __uint_as_float(r3[0]) * score_scale;  // score_scale > 0
-              mh[1] = __uint_as_float(r3[1]) * score_scale;
+              // (block maxima in MFMA units; the log2-domain values are taken
+              // with one fma each where they are used)
+              mh[0] = __uint_as_float(r3[0]);
+              mh[1] = __uint_as_float(r3[1]);
               m_seen = max2(m_seen, max2(mh[0], mh[1], pinf), pinf);
             }
           }
           if (pass == 0 && it == 0) {
             // first tile: the reference is the tile's max over the group's
             // scoring waves
-            if (score) xch_f[wave][lane] = fmaxf(mh[0], mh[1]);
+            if (score) xch_f[wave][lane] = fmaxf(mh[0], mh[1]) * score_scale;  // score_scale > 0
             barrier_lds();
             if (ntiles > 0) {
               float m = -INFINITY;
@@ -989,11 +991,14 @@ void dsa_decode_kernel(DecodeArgs a) {
             // ---- weights, per 16-token block: the block's largest weight of
             // the head maps to [128, 256) (a block with no valid token:
             // exponent -100, weights 0)
+            // block maxima against the reference, log2 domain
+            const float nref = -(mb7 + 7.f);
+            const float x0 = fmaf(mh[0], score_scale, nref), x1 = fmaf(mh[1], score_scale, nref);
             // (an exponent reaches kSlack exactly when the larger block maximum does)
-            overflow |= fmaxf(mh[0], mh[1]) - (mb7 + 7.f) >= kSlack;
+            overflow |= fmaxf(x0, x1) >= kSlack;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-              const float ef = floorf(__builtin_amdgcn_fmed3f(mh[k] - (mb7 + 7.f), -100.f, 100.f));
+              const float ef = floorf(__builtin_amdgcn_fmed3f(k == 0 ? x0 : x1, -100.f, 100.f));
               const float bsub = mb7 + ef;
               const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
               float p[4];
