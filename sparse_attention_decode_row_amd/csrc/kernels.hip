@@ -125,8 +125,13 @@ __device__ __forceinline__ f32x4 mfma_fp8_bscaled(i32x8 a, i32x8 b, int bscale, 
 }
 
 // Four floats -> four FP8 E4M3 codes (round to nearest even), byte i = x_i.
+// (The first conversion writes the low half of a register whose other half
+// the second one overwrites, so that register's prior content is irrelevant:
+// an empty asm hands it over without a copy of 0.)
 __device__ __forceinline__ int pack_fp8x4(float x0, float x1, float x2, float x3) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  int any;
+  asm volatile("" : "=v"(any));
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, any, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
 }
 
