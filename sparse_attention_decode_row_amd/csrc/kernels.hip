@@ -1383,8 +1383,7 @@ void dsa_combine_kernel(DecodeArgs a) {
   const int lane = t % kWave, li = lane & 15, g = lane >> 4;
   const int j = (t / kWave) % kCB, x = (t / (kWave * kCB)) % kGroups;
   const int src = t / (kWave * kCB * kGroups);
-  const int hx = hb * a.heads_per_block + x * 16 + li;
-  if (hx >= a.H) return;
+  const int hx = hb * a.heads_per_block + x * 16 + li;  // (past H: computed, not stored)
   const size_t slot0 = (size_t)rh * a.chunks;
   // (m_c, l_c) of this head: float pairs, heads_per_block pairs per chunk
   const float2* ml = (const float2*)a.part_ml + slot0 * a.heads_per_block + x * 16 + li;
@@ -1430,7 +1429,29 @@ void dsa_combine_kernel(DecodeArgs a) {
   const float inv = bad ? __builtin_nanf("") : (L > 0.f ? a.v_scale / L : 0.f);
   const bf16x4 v = {(__bf16)(o[0] * inv), (__bf16)(o[1] * inv), (__bf16)(o[2] * inv),
                     (__bf16)(o[3] * inv)};
-  *(bf16x4*)(a.out + ((size_t)r * a.H + hx) * D + 16 * (src * kCB + j) + 4 * g) = v;
+  constexpr int kJPerBlock = 256 / kWave;  // column blocks a 256-thread block covers
+  if constexpr (kCB % kJPerBlock == 0) {
+    // The block's results are 16 heads x 64 consecutive columns (its 4 column
+    // blocks of one source wave): staged in LDS, then written as whole
+    // 16-byte pieces, 128 bytes of a head row per 8 lanes.
+    constexpr int kBlkCols = kJPerBlock * 16;
+    constexpr int kStage = 2 * kBlkCols + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[16 * kStage];
+    const int jj = (t / kWave) % kJPerBlock;
+    *(bf16x4*)(stage + li * kStage + 2 * (16 * jj + 4 * g)) = v;
+    __syncthreads();
+    constexpr int kPieces = 2 * kBlkCols / 16;  // 8 per head row
+    if (threadIdx.x < 16 * kPieces) {
+      const int row = threadIdx.x / kPieces, pc = threadIdx.x % kPieces;
+      const int head = hb * a.heads_per_block + x * 16 + row;
+      const int col0 = 16 * (src * kCB + j - jj);  // the block's first column
+      if (head < a.H)
+        *(u32x4*)((uint8_t*)(a.out + ((size_t)r * a.H + head) * D + col0) + 16 * pc) =
+            *(const u32x4*)(stage + row * kStage + 16 * pc);
+    }
+  } else {
+    if (hx < a.H) *(bf16x4*)(a.out + ((size_t)r * a.H + hx) * D + 16 * (src * kCB + j) + 4 * g) = v;
+  }
 }
 
 // Zero a word range (workspace set-up; a kernel rather than a memset so that
