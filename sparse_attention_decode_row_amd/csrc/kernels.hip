@@ -791,21 +791,24 @@ void dsa_decode_kernel(DecodeArgs a) {
 
   // PV operands. The matrix core scales B (the weights) in four blocks of
   // 32 k-positions: bytes 0-15 (then 16-31) of lane groups {0, 1} (then
-  // {2, 3}); lane group G supplies block G's exponent. Each block carries
-  // one 16-token block of the tile, its hi terms and its lo terms, so the 16
+  // {2, 3}); lane group G supplies block G's exponent. Each block carries 16
+  // tokens of the tile, their hi terms and their lo terms, so those 16
   // tokens of a head share one exponent. In lane group G, bytes 16*h ..
-  // 16*h + 7 hold the hi terms of slots 32*h + 8*G .. +7 and bytes 16*h + 8
-  // .. +15 their lo terms: slots 32*h + 8*G + 4*(g & 1) + i come from
-  // scoring lane group g of block 2*h + (G >> 1), byte 4*(g & 1) + i. A (V):
-  // lane group G needs the latent column of those 8 slots twice per half. A
-  // transposing read hands lane li the 8 bytes of its column from 8 rows;
-  // lanes 2k and 2k+1 of the 16-lane group supply row k (column halves 0 and
-  // 1). (Lane groups 0 and 1, read together, cover 16 consecutive slots and
-  // so distinct swizzled chunk positions, as do 2 and 3.)
+  // 16*h + 7 hold the hi terms of slots 32*h + 16*(G & 1) + 8*(G >> 1) .. +7
+  // and bytes 16*h + 8 .. +15 their lo terms. Block 2*h + (G >> 1) thus holds
+  // the 8 slots that scoring lane group g of wave part h holds in each of its
+  // two products, for g = 2*(G >> 1) and g + 1: a lane and the lane 16
+  // apart. Slot 32*h + 16*k + 8*(G >> 1) + 4*(g & 1) + i comes from lane
+  // group g of product k, byte 4*(g & 1) + i. A (V): lane group G needs the
+  // latent column of those 8 slots twice per half. A transposing read hands
+  // lane li the 8 bytes of its column from 8 rows; lanes 2k and 2k+1 of the
+  // 16-lane group supply row k (column halves 0 and 1). (Lane groups 0 and 1,
+  // read together, cover slots 32*h + 0..7 and 32*h + 16..23, which the
+  // swizzle puts at distinct chunk positions, as it does 2 and 3.)
   int vrow[2], vswz[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int slot = 32 * h + 8 * g + (li >> 1);
+    const int slot = 32 * h + 16 * (g & 1) + 8 * (g >> 1) + (li >> 1);
     vrow[h] = slot * D + 8 * (li & 1);
     vswz[h] = tile_swizzle<D>(slot) << 4;
   }
@@ -843,8 +846,8 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Step i scores tile i (scoring waves) and accumulates tile i - 1 (PV
   // waves), between one barrier and the next. The accumulators are touched
   // only by the matrix cores: weights are taken against a fixed per-head
-  // reference (the first tile's max), and each scoring wave's 32 weights of
-  // a head carry their own E8M0 exponent, so a later score may exceed the
+  // reference (the first tile's max), and each block of 16 weights of a
+  // head carries its own E8M0 exponent, so a later score may exceed the
   // reference by up to 2^kSlack without leaving the FP8 range or fp32
   // accumulation. Should a score ever exceed it by more (only with
   // pathological inputs), the chunk is recomputed with the reference set to
@@ -853,12 +856,12 @@ void dsa_decode_kernel(DecodeArgs a) {
   float l_part = 0.f;        // this scoring wave's share of sum_t 2^(s_t - m_ref), per head
   float m_ref = -INFINITY;   // reference of this head's scores (log2 domain)
   float mb7 = -7.f;          // (m_ref, or 0 while it is -inf) - 7
-  float m_seen = -INFINITY;  // exact max of this wave's scores so far (unscaled MFMA units)
+  float m_seen = -INFINITY;  // exact max of the lane pair's scores so far (unscaled MFMA units)
   // After the first pass: recompute the chunk only if some scoring wave saw
   // a score beyond the slack (every wave takes part; two barriers).
   auto redo_needed = [&](bool overflow) {
     if (__any(overflow) && lane == 0) flag_sh = 1;
-    xch_f[wave][lane] = m_seen * score_scale;  // score_scale > 0
+    xch_f[wave][lane] = max_xor32(m_seen) * score_scale;  // score_scale > 0 (m_seen: lane pair's)
     __syncthreads();
     const bool redo = flag_sh != 0;
     if (redo && is_qk) {
@@ -899,7 +902,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
           f32x4 S[2];
-          float mh[2] = {-INFINITY, -INFINITY};  // per 16-token block
+          float mh = -INFINITY;  // max of this lane's weight block
           if (score) {
             const DSA_LDS uint8_t* kt = lds + k_off(it);
             constexpr int kSteps = 2 * kKSteps;
@@ -959,30 +962,21 @@ void dsa_decode_kernel(DecodeArgs a) {
                   if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
             }
             {
-              // Both blocks' maxima over the four lane groups at once. A row
-              // swap of block 0's and block 1's lane maxima leaves rows
-              // (b0 r0, b1 r0, b0 r2, b1 r2) against (b0 r1, b1 r1, b0 r3, b1 r3);
-              // their max, folded across the halves, holds block 0's maximum
-              // in rows 0 and 2 and block 1's in rows 1 and 3, and one more
-              // row swap hands every lane both.
-              const float a0 = max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf);
-              const float a1 = max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf);
-              const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1),
-                                                               false, false);
-              const float d = max_xor32(max2(__uint_as_float(r1[0]), __uint_as_float(r1[1]), pinf), pinf);
-              const auto r3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d),
-                                                               false, false);
-              // (block maxima in MFMA units; the log2-domain values are taken
-              // with one fma each where they are used)
-              mh[0] = __uint_as_float(r3[0]);
-              mh[1] = __uint_as_float(r3[1]);
-              m_seen = max2(m_seen, max2(mh[0], mh[1], pinf), pinf);
+              // The 16 tokens of a weight block are this lane's 8 (4 in each
+              // of its two products) and those of the lane 16 apart: one
+              // lane swap gives the block's maximum (MFMA units; the
+              // log2-domain value is taken with one fma where it is used).
+              const float a = max2(max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf),
+                                   max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf),
+                                   pinf);
+              mh = max_xor16(a, pinf);
+              m_seen = max2(m_seen, mh, pinf);
             }
           }
           if (pass == 0 && it == 0) {
             // first tile: the reference is the tile's max over the group's
             // scoring waves
-            if (score) xch_f[wave][lane] = fmaxf(mh[0], mh[1]) * score_scale;  // score_scale > 0
+            if (score) xch_f[wave][lane] = max_xor32(mh, pinf) * score_scale;  // score_scale > 0
             barrier_lds();
             if (ntiles > 0) {
               float m = -INFINITY;
@@ -993,32 +987,32 @@ void dsa_decode_kernel(DecodeArgs a) {
             }
           }
           if (score) {
-            // ---- weights, per 16-token block: the block's largest weight of
-            // the head maps to [128, 256) (a block with no valid token:
-            // exponent -100, weights 0)
-            // block maxima against the reference, log2 domain
-            const float nref = -(mb7 + 7.f);
-            const float x0 = fmaf(mh[0], score_scale, nref), x1 = fmaf(mh[1], score_scale, nref);
-            // (an exponent reaches kSlack exactly when the larger block maximum does)
-            overflow |= fmaxf(x0, x1) >= kSlack;
+            // ---- weights, per 16-token block (the lane pair's 16 tokens):
+            // the block's largest weight of the head maps to [128, 256) (a
+            // block with no valid token: exponent -100, weights 0)
+            const float x = fmaf(mh, score_scale, -(mb7 + 7.f));  // log2 domain, against the reference
+            overflow |= x >= kSlack;
+            const float ef = floorf(__builtin_amdgcn_fmed3f(x, -100.f, 100.f));
+            const float bsub = mb7 + ef;
+            const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
+            float psum = 0.f;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-              const float ef = floorf(__builtin_amdgcn_fmed3f(k == 0 ? x0 : x1, -100.f, 100.f));
-              const float bsub = mb7 + ef;
-              const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
               float p[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
-              l_part += ((p[0] + p[1]) + (p[2] + p[3])) * __uint_as_float((uint32_t)eb << 23);
+              psum += (p[0] + p[1]) + (p[2] + p[3]);
               int phi, plo;
               split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
-              // block b = 2*part + k: word (g & 1) (hi) and 2 + (g & 1) (lo)
-              // of PV lane group 2*k + (g >> 1), operand half part, head li
-              int* dst = (int*)&xch_p[it & 1][hg][part][(2 * k + (g >> 1)) * 16 + li];
+              // PV lane group 2*(g >> 1) + k, operand half part, head li:
+              // word (g & 1) (hi) and 2 + (g & 1) (lo)
+              int* dst = (int*)&xch_p[it & 1][hg][part][(2 * (g >> 1) + k) * 16 + li];
               dst[g & 1] = phi;
               dst[2 + (g & 1)] = plo;
-              xch_e[it & 1][hg][2 * part + k][li] = eb;  // (every lane group: the same byte)
             }
+            l_part += psum * __uint_as_float((uint32_t)eb << 23);
+            // scale of weight block 2*part + (g >> 1) (the lane pair writes the same byte)
+            xch_e[it & 1][hg][2 * part + (g >> 1)][li] = eb;
           }
         }
       if (pass == 0 && !redo_needed(overflow)) break;
