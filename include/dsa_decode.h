@@ -89,8 +89,9 @@ typedef struct dsa_decode_params {
   int32_t chunk_tokens;
   /* Heads per workgroup: DSA_DECODE_LAYOUT_AUTO (0) lets the planner choose
    * (16 when num_q_heads <= 16, else 32); DSA_DECODE_LAYOUT_HEADS32 (1):
-   * blocks of up to 32 heads, eight waves per workgroup;
-   * DSA_DECODE_LAYOUT_HEADS16 (2): blocks of up to 16 heads, four waves.
+   * blocks of up to 32 heads, eight waves per workgroup (two scoring waves
+   * of 32 tokens per 16-head group); DSA_DECODE_LAYOUT_HEADS16 (2): blocks
+   * of up to 16 heads, also eight waves (four scoring waves of 16 tokens).
    * The head blocks of a row read the same latent rows through the same L2.
    * The result does not depend on it. */
   int32_t layout;

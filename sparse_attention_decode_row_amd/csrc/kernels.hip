@@ -295,14 +295,19 @@ struct DecodeArgs {
 // wait starts, so it ends within microseconds unless a counter is broken.
 constexpr uint64_t kMergeWaitTicks = 10000000;
 
-// Waves of a workgroup: per 16-head group two scoring waves, each taking
-// 32 tokens of a 64-token tile (QK^T and the softmax weights), and as many
-// PV waves, which split the latent columns between them and accumulate
-// every head group. Scoring wave w and PV wave w + kWaves/2 share a SIMD,
-// so the vector work of one runs under the matrix work of the other.
+// Waves of a workgroup: per 16-head group kParts scoring waves, each taking
+// a 64 / kParts-token share of a 64-token tile (QK^T and the softmax
+// weights), and as many PV waves, which split the latent columns between
+// them and accumulate every head group. Scoring wave w and PV wave
+// w + kWaves/2 share a SIMD, so the vector work of one runs under the
+// matrix work of the other.
 constexpr int kTile = 64;     // tokens per staged tile
 constexpr int kBuffers = 4;   // tile buffers: two in use, two in flight
-constexpr int kParts = 2;     // scoring waves per head group (32 tokens each)
+// Scoring waves per 16-head group: two (32 tokens of a tile each) with two
+// groups per workgroup, four (16 tokens each) with one, so that a workgroup
+// always has eight waves, two per SIMD.
+__host__ __device__ constexpr int parts_of(int groups) { return groups == 1 ? 4 : 2; }
+__host__ __device__ constexpr int waves_of(int groups) { return 2 * parts_of(groups) * groups; }
 
 // kGroups: 16-head groups per workgroup (1 or 2).
 // kSplitV: V is read from its own buffer (two K and two V tile buffers;
@@ -316,8 +321,10 @@ constexpr int kParts = 2;     // scoring waves per head group (32 tokens each)
 // side in its 128-deep k dimension) and staged in its own region of each
 // tile buffer; the values and the output are the latent alone.
 template <int D, int kGroups, bool kSplitV, int kRope = 0>
-__global__ __launch_bounds__(4 * kGroups * kWave, 1)
+__global__ __launch_bounds__(waves_of(kGroups) * kWave, 1)
 void dsa_decode_kernel(DecodeArgs a) {
+  constexpr int kParts = parts_of(kGroups);
+  constexpr int kBPW = 4 / kParts;                  // 16-token blocks per scoring wave
   constexpr int kQKWaves = kParts * kGroups;
   constexpr int kPVWaves = kQKWaves;
   constexpr int kWaves = kQKWaves + kPVWaves;
@@ -426,7 +433,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // group w % kGroups, k-steps ks = 4*i + w / kGroups, and the terms are
   // exchanged through tile buffers 2 and 3 (4 KiB per group and k-step). A
   // single k-step is loaded by every wave.
-  constexpr int kQWaysPerGroup = kWaves / kGroups;  // 4
+  constexpr int kQWaysPerGroup = kWaves / kGroups;  // 4, or 8 with one group
   const int qsub = wave / kGroups;
   const int q_head = hb * a.heads_per_block + hg * 16 + li;
   const bool q_ok = q_head < a.H;
@@ -777,38 +784,48 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
   }
 
-  // K operand addresses of a scoring wave. It scores blocks b = 2*part + k
-  // (k < 2) of 16 slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at chunk
-  // position (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that position
-  // is 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ k) & 1)), so four per-lane
-  // offsets plus compile-time immediates cover every read.
+  // K operand addresses of a scoring wave. It scores blocks b = kBPW*part +
+  // k (k < kBPW) of 16 slots. Slot 16*b + li, chunk 8*ks + 2*g + h sits at
+  // chunk position (chunk ^ swizzle); with swizzle = li ^ 8*(b & 1) that
+  // position is 16*(ks >> 1) + (((2*g + h) ^ li) ^ 8*((ks ^ b) & 1)), so four
+  // per-lane offsets (b's parity folded in when a wave has one block) plus
+  // compile-time immediates cover every read.
   int kofs[2][2];
+  const int bpar = kBPW == 1 ? (part & 1) : 0;
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      kofs[p][h] = 32 * D * part + li * D + 16 * ((((2 * g + h) ^ li) ^ (8 * p)) & kChunkMask);
+      kofs[p][h] = 16 * kBPW * D * part + li * D +
+                   16 * ((((2 * g + h) ^ li) ^ (8 * (p ^ bpar))) & kChunkMask);
 
   // PV operands. The matrix core scales B (the weights) in four blocks of
   // 32 k-positions: bytes 0-15 (then 16-31) of lane groups {0, 1} (then
   // {2, 3}); lane group G supplies block G's exponent. Each block carries 16
   // tokens of the tile, their hi terms and their lo terms, so those 16
   // tokens of a head share one exponent. In lane group G, bytes 16*h ..
-  // 16*h + 7 hold the hi terms of slots 32*h + 16*(G & 1) + 8*(G >> 1) .. +7
-  // and bytes 16*h + 8 .. +15 their lo terms. Block 2*h + (G >> 1) thus holds
-  // the 8 slots that scoring lane group g of wave part h holds in each of its
-  // two products, for g = 2*(G >> 1) and g + 1: a lane and the lane 16
-  // apart. Slot 32*h + 16*k + 8*(G >> 1) + 4*(g & 1) + i comes from lane
-  // group g of product k, byte 4*(g & 1) + i. A (V): lane group G needs the
-  // latent column of those 8 slots twice per half. A transposing read hands
-  // lane li the 8 bytes of its column from 8 rows; lanes 2k and 2k+1 of the
-  // 16-lane group supply row k (column halves 0 and 1). (Lane groups 0 and 1,
-  // read together, cover slots 32*h + 0..7 and 32*h + 16..23, which the
-  // swizzle puts at distinct chunk positions, as it does 2 and 3.)
+  // 16*h + 7 hold the hi terms of 8 slots and bytes 16*h + 8 .. +15 their lo
+  // terms:
+  // - two blocks per scoring wave: slots 32*h + 16*(G & 1) + 8*(G >> 1) ..
+  //   +7. Block 2*h + (G >> 1) thus holds the 8 slots that scoring lane
+  //   group g of wave part h holds in each of its two products, for
+  //   g = 2*(G >> 1) and g + 1: a lane and the lane 16 apart. Slot 32*h +
+  //   16*k + 8*(G >> 1) + 4*(g & 1) + i comes from lane group g of product
+  //   k, byte 4*(g & 1) + i.
+  // - one block per scoring wave: slots 32*h + 8*G .. +7, so block 2*h +
+  //   (G >> 1) is the 16 slots of scoring wave part 2*h + (G >> 1). Slot
+  //   16*part + 4*g + i comes from its lane group g, in PV lane group
+  //   2*(part & 1) + (g >> 1), byte 4*(g & 1) + i.
+  // A (V): lane group G needs the latent column of those 8 slots twice per
+  // half. A transposing read hands lane li the 8 bytes of its column from 8
+  // rows; lanes 2k and 2k+1 of the 16-lane group supply row k (column halves
+  // 0 and 1). (The slots that lane groups 0 and 1, and 2 and 3, read
+  // together sit at distinct chunk positions under the swizzle.)
   int vrow[2], vswz[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int slot = 32 * h + 16 * (g & 1) + 8 * (g >> 1) + (li >> 1);
+    const int slot = kBPW == 2 ? 32 * h + 16 * (g & 1) + 8 * (g >> 1) + (li >> 1)
+                               : 32 * h + 8 * g + (li >> 1);
     vrow[h] = slot * D + 8 * (li & 1);
     vswz[h] = tile_swizzle<D>(slot) << 4;
   }
@@ -901,11 +918,11 @@ void dsa_decode_kernel(DecodeArgs a) {
 
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
-          f32x4 S[2];
+          f32x4 S[kBPW];
           float mh = -INFINITY;  // max of this lane's weight block
           if (score) {
             const DSA_LDS uint8_t* kt = lds + k_off(it);
-            constexpr int kSteps = 2 * kKSteps;
+            constexpr int kSteps = kBPW * kKSteps;
             auto load_k = [&](int s) -> i32x8 {
               const int k = s / kKSteps, ks = s % kKSteps;
               i32x8 kop = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -919,10 +936,10 @@ void dsa_decode_kernel(DecodeArgs a) {
               }
               return kop;
             };
-            // Rope tail of block k: slot 32*part + 16*k + li, bytes
+            // Rope tail of block k: slot 16*(kBPW*part + k) + li, bytes
             // 32*(g & 1) .. + 31 (chunks XOR-permuted by slot bits 2-3).
             auto load_tail = [&](int k) -> i32x8 {
-              const DSA_LDS uint8_t* tb = kt + kTileBytes + (32 * part + 16 * k + li) * kRope;
+              const DSA_LDS uint8_t* tb = kt + kTileBytes + (16 * (kBPW * part + k) + li) * kRope;
               const int sw = (li >> 2) & 3, c = 2 * (g & 1);
               const u32x4 lo = *(const DSA_LDS u32x4*)(tb + 16 * (c ^ sw));
               const u32x4 hi = *(const DSA_LDS u32x4*)(tb + 16 * ((c + 1) ^ sw));
@@ -952,24 +969,32 @@ void dsa_decode_kernel(DecodeArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_s_setprio(0);
-            // The lane holds head li at slots 32*part + 16*k + 4*g + i.
+            // Vector instructions read (or mask) the scores next. The matrix
+            // core's result of this product shape is readable 11 wait states
+            // after issue, and nothing interlocks; the compiler's own hazard
+            // padding has been seen to fall short here (3 wait states), so
+            // the padding is explicit.
+            asm volatile("s_nop 7\n\ts_nop 2" ::: "memory");
+            // The lane holds head li at slots 16*(kBPW*part + k) + 4*g + i.
             const int nvalid = n - it * kTile;
             if (__builtin_expect(nvalid < kTile, 0)) {
 #pragma unroll
-              for (int k = 0; k < 2; ++k)
+              for (int k = 0; k < kBPW; ++k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                  if (token_of_slot(32 * part + 16 * k + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
+                  if (token_of_slot(16 * (kBPW * part + k) + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
             }
             {
-              // The 16 tokens of a weight block are this lane's 8 (4 in each
-              // of its two products) and those of the lane 16 apart: one
-              // lane swap gives the block's maximum (MFMA units; the
-              // log2-domain value is taken with one fma where it is used).
-              const float a = max2(max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf),
-                                   max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf),
-                                   pinf);
+              // A weight block's 16 tokens: with two products per wave, this
+              // lane's 8 (4 in each) and those of the lane 16 apart (one lane
+              // swap); with one, the 4 of each lane group (two swaps). The
+              // maximum stays in MFMA units; the log2-domain value is taken
+              // with one fma where it is used.
+              float a = max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf);
+              if constexpr (kBPW == 2)
+                a = max2(a, max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf), pinf);
               mh = max_xor16(a, pinf);
+              if constexpr (kBPW == 1) mh = max_xor32(mh, pinf);
               m_seen = max2(m_seen, mh, pinf);
             }
           }
@@ -987,9 +1012,9 @@ void dsa_decode_kernel(DecodeArgs a) {
             }
           }
           if (score) {
-            // ---- weights, per 16-token block (the lane pair's 16 tokens):
-            // the block's largest weight of the head maps to [128, 256) (a
-            // block with no valid token: exponent -100, weights 0)
+            // ---- weights, per 16-token block: the block's largest weight of
+            // the head maps to [128, 256) (a block with no valid token:
+            // exponent -100, weights 0)
             const float x = fmaf(mh, score_scale, -(mb7 + 7.f));  // log2 domain, against the reference
             overflow |= x >= kSlack;
             const float ef = floorf(__builtin_amdgcn_fmed3f(x, -100.f, 100.f));
@@ -997,22 +1022,25 @@ void dsa_decode_kernel(DecodeArgs a) {
             const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
             float psum = 0.f;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
+            for (int k = 0; k < kBPW; ++k) {
               float p[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
               psum += (p[0] + p[1]) + (p[2] + p[3]);
               int phi, plo;
               split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
-              // PV lane group 2*(g >> 1) + k, operand half part, head li:
-              // word (g & 1) (hi) and 2 + (g & 1) (lo)
-              int* dst = (int*)&xch_p[it & 1][hg][part][(2 * (g >> 1) + k) * 16 + li];
+              // head li, word (g & 1) (hi) and 2 + (g & 1) (lo) of PV lane
+              // group 2*(g >> 1) + k, operand half part (two products), or
+              // of lane group 2*(part & 1) + (g >> 1), half part >> 1 (one)
+              int* dst = kBPW == 2 ? (int*)&xch_p[it & 1][hg][part][(2 * (g >> 1) + k) * 16 + li]
+                                   : (int*)&xch_p[it & 1][hg][part >> 1][(2 * (part & 1) + (g >> 1)) * 16 + li];
               dst[g & 1] = phi;
               dst[2 + (g & 1)] = plo;
             }
             l_part += psum * __uint_as_float((uint32_t)eb << 23);
-            // scale of weight block 2*part + (g >> 1) (the lane pair writes the same byte)
-            xch_e[it & 1][hg][2 * part + (g >> 1)][li] = eb;
+            // scale of weight block 2*part + (g >> 1), or part (the lanes
+            // that share the block write the same byte)
+            xch_e[it & 1][hg][kBPW == 2 ? 2 * part + (g >> 1) : part][li] = eb;
           }
         }
       if (pass == 0 && !redo_needed(overflow)) break;
@@ -1255,10 +1283,13 @@ void dsa_decode_kernel(DecodeArgs a) {
   __syncthreads();
   const float poison = flag_sh == 2 && !sticky_bad ? 0.f : __builtin_nanf("");
   // Wave w merges units (group x, column block j) half*kU .. half*kU + kU - 1
-  // of PV wave src = w % kPVWaves's register order (unit = x * kCB + j).
-  constexpr int kU = kGroups * kCB / 2;
-  static_assert(kU >= 1 && 2 * kU == kGroups * kCB && 2 * kPVWaves == kWaves, "merge split");
+  // of PV wave src = w % kPVWaves's register order (unit = x * kCB + j); a
+  // PV wave's single unit is merged by the first half of the waves alone.
+  constexpr int kHalves = kGroups * kCB >= 2 ? 2 : 1;
+  constexpr int kU = kGroups * kCB / kHalves;
+  static_assert(kU >= 1 && kHalves * kU == kGroups * kCB && 2 * kPVWaves == kWaves, "merge split");
   const int src = wave % kPVWaves, half = wave / kPVWaves;
+  if (half >= kHalves) return;  // (no barrier follows)
   auto unit_x = [&](int u) { return (half * kU + u) / kCB; };
   auto unit_j = [&](int u) { return (half * kU + u) % kCB; };
   // Online log-sum-exp merge over batches of kB chunks in fixed order
@@ -1363,7 +1394,7 @@ __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 template <int D, int kGroups>
 __global__ __launch_bounds__(256)
 void dsa_combine_kernel(DecodeArgs a) {
-  constexpr int kPVWaves = kParts * kGroups;
+  constexpr int kPVWaves = parts_of(kGroups) * kGroups;
   constexpr int kCB = D / 16 / kPVWaves;
   constexpr int kUnits = kPVWaves * kGroups * kCB * kWave;  // float4s per chunk partial
   constexpr int kBlocksPerUnit = kUnits / 256;
@@ -1461,7 +1492,7 @@ __global__ void dsa_zero_kernel(int32_t* p, size_t n) {
 template <int D, int kGroups>
 hipError_t launch_g(bool split_v, bool rope, bool combine, dim3 grid, hipStream_t st,
                     const DecodeArgs& args) {
-  const dim3 block(4 * kGroups * kWave);
+  const dim3 block(waves_of(kGroups) * kWave);
   if (rope) {
     if constexpr (D == 512)
       hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false, 64>), grid, block, 0, st, args);
