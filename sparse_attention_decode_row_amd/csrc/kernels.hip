@@ -1152,7 +1152,9 @@ void dsa_decode_kernel(DecodeArgs a) {
     // The block's output rows are contiguous in `out`: they are staged in
     // the (now idle) tile buffers as bf16, rows 2*D + 16 bytes apart so that
     // the 16 rows one staging store touches fall in distinct banks, and then
-    // written as whole 16-byte pieces, consecutive lanes on consecutive bytes.
+    // written as whole 16-byte pieces, consecutive lanes on consecutive bytes,
+    // with streaming stores (nothing here reads them again, so they need not
+    // wait in L2 for the end-of-kernel write-back).
     constexpr int kStageRow = 2 * D + 16;
     static_assert(kGroups * 16 * kStageRow <= kSmemBytes, "output staging");
     if (!is_qk)
@@ -1173,7 +1175,8 @@ void dsa_decode_kernel(DecodeArgs a) {
     constexpr int kPieces = 2 * D / 16;  // 16-byte pieces per row
     for (int i = tid; i < rows * kPieces; i += kThreads) {
       const int row = i / kPieces, pc = i - row * kPieces;
-      *(u32x4*)(ob + (size_t)row * (2 * D) + 16 * pc) = *(const u32x4*)(smem + row * kStageRow + 16 * pc);
+      __builtin_nontemporal_store(*(const u32x4*)(smem + row * kStageRow + 16 * pc),
+                                  (u32x4*)(ob + (size_t)row * (2 * D) + 16 * pc));
     }
     return;
   }
@@ -1471,8 +1474,8 @@ void dsa_combine_kernel(DecodeArgs a) {
       const int head = hb * a.heads_per_block + x * 16 + row;
       const int col0 = 16 * (src * kCB + j - jj);  // the block's first column
       if (head < a.H)
-        *(u32x4*)((uint8_t*)(a.out + ((size_t)r * a.H + head) * D + col0) + 16 * pc) =
-            *(const u32x4*)(stage + row * kStage + 16 * pc);
+        __builtin_nontemporal_store(*(const u32x4*)(stage + row * kStage + 16 * pc),  // (streaming)
+                                    (u32x4*)((uint8_t*)(a.out + ((size_t)r * a.H + head) * D + col0) + 16 * pc));
     }
   } else {
     if (hx < a.H) *(bf16x4*)(a.out + ((size_t)r * a.H + hx) * D + 16 * (src * kCB + j) + 4 * g) = v;
