@@ -331,13 +331,17 @@ void dsa_decode_kernel(DecodeArgs a) {
   constexpr int kThreads = kWave * kWaves;
   static_assert(kRope == 0 || (kRope == 64 && D == 512 && !kSplitV), "rope tail: 512 + 64, one K/V buffer");
   constexpr int kRowBytes = D + kRope;              // bytes of a cached token
-  constexpr int kTileBytes = kTile * D;             // latent region of a tile buffer
-  constexpr int kTailBytes = kTile * kRope;         // tail region, after the latent
-  constexpr int kBufBytes = kTileBytes + kTailBytes;
-  constexpr int kSmemBytes = kBuffers * kBufBytes;
-  // rows one workgroup takes (its latent-row table is in LDS; the tail's
-  // region leaves room for 1024)
-  constexpr int kMaxChunk = kRope ? kMaxChunkTokens / 2 : kMaxChunkTokens;
+  constexpr int kTileBytes = kTile * D;             // a tile buffer: the tile's latent rows
+  constexpr int kBufBytes = kTileBytes;
+  // Rope tails: only the scoring waves read them, in the step that scores
+  // the tile, so three tail slots after the tile buffers serve the tile
+  // being scored and the two in flight (the slot tile i + 2 loads into held
+  // tile i - 1, scored in the step before).
+  constexpr int kTailBytes = kTile * kRope;         // one tile's tails
+  constexpr int kTailSlots = kRope ? 3 : 0;
+  constexpr int kTailOff = kBuffers * kBufBytes;
+  constexpr int kSmemBytes = kBuffers * kBufBytes + kTailSlots * kTailBytes;
+  constexpr int kMaxChunk = kMaxChunkTokens;        // rows one workgroup takes (its row table is in LDS)
   constexpr int kTailInstr = kTailBytes / (16 * kWave);  // tail DMAs per tile (one per wave)
   constexpr int kKSteps = (D + 127) / 128;          // QK MFMA steps over the latent width
   constexpr int kDBlocks = D / 16;                  // 16-column blocks of the output
@@ -669,13 +673,14 @@ void dsa_decode_kernel(DecodeArgs a) {
   // token the latent region holds at that slot. The tail's 16-byte chunks are
   // XOR-permuted by bits 2-3 of the slot, so the 16 slots one MFMA operand
   // read touches land in distinct bank groups.
-  auto tail_dma = [&](int tile, int buf_off) {
+  auto tail_off = [&](int tile) { return kTailOff + (tile % 3) * kTailBytes; };
+  auto tail_dma = [&](int tile) {
     if (kRope && wave < kTailInstr && tile < ntiles) {
       const int slot = 16 * wave + (lane >> 2);
       const uint32_t row = rows_l[tile * kTile + token_of_slot(slot)];
       const uint32_t chunk = (uint32_t)((lane & 3) ^ ((slot >> 2) & 3)) << 4;
       dma16(a.k_cache + (uint64_t)row * kRowBytes + D + chunk,
-            (DSA_LDS void*)(lds + buf_off + kTileBytes + wave * 16 * kWave));
+            (DSA_LDS void*)(lds + tail_off(tile) + wave * 16 * kWave));
     }
   };
   // Tile it has landed for this wave once only the DMAs of the next tile
@@ -691,9 +696,9 @@ void dsa_decode_kernel(DecodeArgs a) {
   auto issue_first = [&]() {
     if (dma_wave) {
       if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
-      tail_dma(0, k_off(0));
+      tail_dma(0);
       if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
-      tail_dma(1, k_off(1));
+      tail_dma(1);
     }
   };
 
@@ -914,7 +919,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           uint32_t c0 = dma_c0;
           asm volatile("" : "+v"(c0));
           if (dma_wave) dma_rows(it, drow);
-          if (!kSplitV) tail_dma(it + 2, k_off(it + 2));
+          if (!kSplitV) tail_dma(it + 2);
 
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
@@ -939,7 +944,7 @@ void dsa_decode_kernel(DecodeArgs a) {
             // Rope tail of block k: slot 16*(kBPW*part + k) + li, bytes
             // 32*(g & 1) .. + 31 (chunks XOR-permuted by slot bits 2-3).
             auto load_tail = [&](int k) -> i32x8 {
-              const DSA_LDS uint8_t* tb = kt + kTileBytes + (16 * (kBPW * part + k) + li) * kRope;
+              const DSA_LDS uint8_t* tb = lds + tail_off(it) + (16 * (kBPW * part + k) + li) * kRope;
               const int sw = (li >> 2) & 3, c = 2 * (g & 1);
               const u32x4 lo = *(const DSA_LDS u32x4*)(tb + 16 * (c ^ sw));
               const u32x4 hi = *(const DSA_LDS u32x4*)(tb + 16 * ((c + 1) ^ sw));
@@ -1065,7 +1070,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           asm volatile("" : "+v"(c0));
           if (dma_wave) dma_rows(it, drow);
           // (with 16-head blocks PV waves also move a quarter of the tail)
-          if (!kSplitV) tail_dma(it + 2, k_off(it + 2));
+          if (!kSplitV) tail_dma(it + 2);
           if (it == 0) {
 #pragma unroll
             for (int d = 0; d < kNd; ++d) dma_step(it, d, drow, c0);

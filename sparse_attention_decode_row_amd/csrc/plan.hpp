@@ -16,10 +16,11 @@ constexpr int kTileTokens = 64;  // chunk sizes are multiples of this
 // Largest chunk one workgroup handles (its latent-row table lives in LDS:
 // 2048 x 4 B = 8 KiB).
 constexpr int kMaxChunkTokens = 2048;
-// A plan's largest chunk: a workgroup holds its latent-row table in LDS, and
-// with a rope tail the tail's staging area leaves room for half as many.
+// A plan's largest chunk: a workgroup holds its latent-row table in LDS
+// (with or without a rope tail).
 inline int max_chunk_tokens(const dsa_decode_params& p) {
-  return p.qk_rope_dim ? kMaxChunkTokens / 2 : kMaxChunkTokens;
+  (void)p;
+  return kMaxChunkTokens;
 }
 // Bytes of one cached token.
 inline uint64_t token_bytes(const dsa_decode_params& p) {

@@ -70,7 +70,7 @@ def plan(native, **kw):
     (dict(qk_rope_dim=64, cache_stride_bytes=64 * 512), -1, "smaller than one page"),
     (dict(qk_rope_dim=64, cache_stride_bytes=64 * 576 + 512), -1,
      "not a multiple of the token's 576 bytes"),
-    (dict(qk_rope_dim=64, chunk_tokens=2048), -1, "up to 1024"),
+    (dict(qk_rope_dim=64, chunk_tokens=4096), -1, "up to 2048"),
     (dict(flags=8), -1, "unknown flags"),
     (dict(block_table_stride=100), -1, "block-table entries per row"),
     (dict(sm_scale=float("inf")), -1, "sm_scale must be finite"),
@@ -103,18 +103,20 @@ def test_no_gpu_means_device_error(native):
 
 
 def test_rope_tail_plans(native):
-    # 576-byte tokens: pages of block_size such tokens by default, at most
-    # 1024 tokens per workgroup, so a 2048-wide row is split in two
+    # 576-byte tokens: pages of block_size such tokens by default; a
+    # workgroup takes up to 2048 of them like 512-byte tokens (the tails sit
+    # in a three-slot ring beside the tile buffers), so the long-context
+    # shape keeps one workgroup per (row, head block)
     p = plan(native, qk_rope_dim=64).info()
     assert p["qk_rope_dim"] == 64
-    assert p["chunk_tokens"] == 1024 and p["chunks_per_row"] == 2
-    assert p["merges_chunks"] == 1
+    assert p["chunk_tokens"] == 2048 and p["chunks_per_row"] == 1
+    assert p["merges_chunks"] == 0 and p["workgroups"] == 256
     q = plan(native, qk_rope_dim=64, cache_stride_bytes=64 * 576 * 2).info()
-    assert q["chunks_per_row"] == 2
-    # the in-kernel merge's lead must still leave chunk 0 within 1024 tokens
+    assert q["chunks_per_row"] == 1
+    # a forced split and the in-kernel merge's lead stay within 2048 tokens
     m = plan(native, qk_rope_dim=64, num_rows=32, max_seq_len=8192, block_table_stride=128,
              merge_in_kernel=True).info()
-    assert m["chunk_tokens"] + m["chunk_lead"] <= 1024
+    assert m["chunks_per_row"] > 1 and m["chunk_tokens"] + m["chunk_lead"] <= 2048
 
 
 def test_masked_reference_refuses_rope_tail(native):

@@ -38,7 +38,7 @@ def test_glm_shaped_with_rope_tail(H, in_kernel):
     _announce("glm + rope tail", rows=wl.rows, heads=wl.heads, in_kernel=in_kernel)
     run = H.run_gpu(wl, merge_in_kernel=in_kernel)
     print("plan", run.info)
-    assert run.info["qk_rope_dim"] == 64 and run.info["chunk_tokens"] <= 1024
+    assert run.info["qk_rope_dim"] == 64 and run.info["chunk_tokens"] <= 2048
     H.check_selection(wl, run)
     want = H.oracle_rows(wl, range(wl.rows))
     err = H.normwise_err(run.out, want)
@@ -52,11 +52,15 @@ def test_glm_shaped_with_rope_tail(H, in_kernel):
     (3, 64, 2, 256, False),
     (4, 24, 1, 64, True),
     (5, 128, 0, 1024, False),
+    (6, 32, 1, 2048, False),   # one workgroup takes 2048 tokens: the tail ring wraps ten times
+    (7, 16, 2, 2048, True),
 ])
 def test_random_shapes_with_rope_tail(H, seed, heads, layout, ct, shared):
     rng = np.random.default_rng(900 + seed)
-    base = WL.random_case(rng, rows=5, heads=heads, D=512, block_size=64, max_len=3000,
-                          width=1500, shared_table=shared)
+    wide = ct == 2048
+    base = WL.random_case(rng, rows=5, heads=heads, D=512, block_size=64,
+                          max_len=6000 if wide else 3000, width=2048 if wide else 1500,
+                          shared_table=shared)
     wl = WL.with_rope_tail(base, seed=seed)
     _announce("rope random", seed=seed, heads=heads, layout=layout, ct=ct, shared=shared)
     run = H.run_gpu(wl, chunk_tokens=ct, layout=layout)
