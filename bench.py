@@ -61,6 +61,9 @@ def parse():
                          "afterwards) or writes it (they hold dirty lines, which the decode's "
                          "own reads then push out to HBM)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
+    ap.add_argument("--layout", type=int, default=0, choices=[0, 1, 2],
+                    help="head blocks: 0 the planner's choice, 1 blocks of 32 heads, "
+                         "2 blocks of 16")
     ap.add_argument("--rope-tail", action="store_true",
                     help="576-byte tokens: the latent plus a 64-byte rope tail (q 576 wide, "
                          "scores over 576, values over 512); no CPU baseline")
@@ -141,7 +144,8 @@ def main():
                     block_size=base.block_size, index_kpool=base.kpool, sel_width=W,
                     block_table_stride=base.bt_stride, max_seq_len=base.max_seq_len,
                     sm_scale=base.sm_scale, cache_stride_bytes=base.cache_stride_bytes,
-                    chunk_tokens=args.chunk_tokens, merge_in_kernel=args.merge_in_kernel,
+                    chunk_tokens=args.chunk_tokens, layout=args.layout,
+                    merge_in_kernel=args.merge_in_kernel,
                     qk_rope_dim=rope, rows_per_sequence=rows_per_seq, device=0)
     ws = plan.new_workspace(0)
     info = plan.info()
