@@ -61,9 +61,9 @@ def parse():
                          "afterwards) or writes it (they hold dirty lines, which the decode's "
                          "own reads then push out to HBM)")
     ap.add_argument("--chunk-tokens", type=int, default=0)
-    ap.add_argument("--layout", type=int, default=0, choices=[0, 1, 2],
+    ap.add_argument("--layout", type=int, default=0, choices=[0, 1, 2, 3],
                     help="head blocks: 0 the planner's choice, 1 blocks of 32 heads, "
-                         "2 blocks of 16")
+                         "2 blocks of 16, 3 blocks of 64")
     ap.add_argument("--rope-tail", action="store_true",
                     help="576-byte tokens: the latent plus a 64-byte rope tail (q 576 wide, "
                          "scores over 576, values over 512); no CPU baseline")

@@ -88,10 +88,16 @@ typedef struct dsa_decode_params {
    * that the result does not depend on the split). */
   int32_t chunk_tokens;
   /* Heads per workgroup: DSA_DECODE_LAYOUT_AUTO (0) lets the planner choose
-   * (16 when num_q_heads <= 16, else 32); DSA_DECODE_LAYOUT_HEADS32 (1):
+   * (16 when num_q_heads <= 16; 64 when num_rows * ceil(num_q_heads / 64)
+   * workgroups already give every compute unit one and 64-head blocks are
+   * allowed, see below; else 32); DSA_DECODE_LAYOUT_HEADS32 (1):
    * blocks of up to 32 heads, eight waves per workgroup (two scoring waves
    * of 32 tokens per 16-head group); DSA_DECODE_LAYOUT_HEADS16 (2): blocks
-   * of up to 16 heads, also eight waves (four scoring waves of 16 tokens).
+   * of up to 16 heads, also eight waves (four scoring waves of 16 tokens);
+   * DSA_DECODE_LAYOUT_HEADS64 (3): blocks of up to 64 heads, eight waves
+   * (one scoring wave of the whole tile per 16-head group), for
+   * kv_lora_rank 512 without a rope tail or DSA_DECODE_FLAG_MERGE_IN_KERNEL
+   * (otherwise DSA_DECODE_ERR_UNSUPPORTED).
    * The head blocks of a row read the same latent rows through the same L2.
    * The result does not depend on it. */
   int32_t layout;
@@ -124,6 +130,7 @@ typedef struct dsa_decode_params {
 #define DSA_DECODE_LAYOUT_AUTO 0
 #define DSA_DECODE_LAYOUT_HEADS32 1
 #define DSA_DECODE_LAYOUT_HEADS16 2
+#define DSA_DECODE_LAYOUT_HEADS64 3
 
 /* flags: every launch also writes the normalised selection (ids, counts and
  * byte offsets) into the workspace, for dsa_decode_read_selection. Off by
@@ -159,7 +166,7 @@ typedef struct dsa_decode_plan_info {
                             * are merged in the kernel (it then finishes last
                             * and merges); the last chunk has that many fewer */
   uint64_t workspace_bytes;
-  int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32 or _HEADS16 (resolved) */
+  int32_t layout;          /* DSA_DECODE_LAYOUT_HEADS32, _HEADS16 or _HEADS64 (resolved) */
   int32_t heads_per_block; /* 32 or 16 */
   int32_t rows_per_sequence; /* rows co-scheduled on one XCD (1: none) */
   int32_t flags;           /* params.flags */

@@ -303,13 +303,13 @@ constexpr uint64_t kMergeWaitTicks = 10000000;
 // matrix work of the other.
 constexpr int kTile = 64;     // tokens per staged tile
 constexpr int kBuffers = 4;   // tile buffers: two in use, two in flight
-// Scoring waves per 16-head group: two (32 tokens of a tile each) with two
-// groups per workgroup, four (16 tokens each) with one, so that a workgroup
-// always has eight waves, two per SIMD.
-__host__ __device__ constexpr int parts_of(int groups) { return groups == 1 ? 4 : 2; }
+// Scoring waves per 16-head group: four (16 tokens of a tile each) with one
+// group per workgroup, two (32 tokens each) with two, one (the whole tile)
+// with four, so that a workgroup always has eight waves, two per SIMD.
+__host__ __device__ constexpr int parts_of(int groups) { return 4 / groups; }
 __host__ __device__ constexpr int waves_of(int groups) { return 2 * parts_of(groups) * groups; }
 
-// kGroups: 16-head groups per workgroup (1 or 2).
+// kGroups: 16-head groups per workgroup (1, 2 or 4).
 // kSplitV: V is read from its own buffer (two K and two V tile buffers;
 // the next tile's K and this tile's V load while the current ones are
 // consumed). Otherwise K and V are the same bytes, in four tile buffers:
@@ -325,6 +325,10 @@ __global__ __launch_bounds__(waves_of(kGroups) * kWave, 1)
 void dsa_decode_kernel(DecodeArgs a) {
   constexpr int kParts = parts_of(kGroups);
   constexpr int kBPW = 4 / kParts;                  // 16-token blocks per scoring wave
+  // Weight blocks (16 tokens of a head under one exponent) per scoring lane:
+  // with two or four products a block pairs two products' halves (a lane and
+  // the lane 16 apart), so four products make two such sets.
+  constexpr int kWB = kBPW == 4 ? 2 : 1;
   constexpr int kQKWaves = kParts * kGroups;
   constexpr int kPVWaves = kQKWaves;
   constexpr int kWaves = kQKWaves + kPVWaves;
@@ -454,7 +458,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   auto own_ks = [&](int i) { return kShareQ ? kQWaysPerGroup * i + qsub : i; };
   u32x4 qraw[kKOwn][4];
   u32x4 qtraw[4];
-  static_assert(kKOwn == 1, "one k-step of the query per wave (four 16-byte loads)");
+  static_assert(kKOwn <= 2, "at most two k-steps of the query per wave (four 16-byte loads each)");
   auto load_q = [&]() {
     const uint16_t* qrow = a.q + ((size_t)r * a.H + (q_ok ? q_head : 0)) * kRowBytes;
 #pragma unroll
@@ -768,7 +772,36 @@ void dsa_decode_kernel(DecodeArgs a) {
   // one MFMA per block adds K_tail . (hi + lo). Lane group G takes the
   // words that lane group G % 2 converted, hi for G < 2 and lo otherwise.
   i32x8 qtail = {0, 0, 0, 0, 0, 0, 0, 0};
+  // Read by the scoring waves before the first barrier of the loop (after
+  // it the gather overwrites the area). With four head groups they are read
+  // at the start of the scoring branch: held from here instead, across the
+  // branch, they crowded the PV branch's registers (71 registers spilled,
+  // reloaded inside the loop with a wait for every gather in flight).
+  // Otherwise they are read here (the same reads written out below: wrapped
+  // in this lambda the compiler builds their addresses differently).
+  auto load_qterms = [&]() {
   if constexpr (kShareQ) {
+    {
+      const u32x4* qx = (const u32x4*)(smem + kQxOff);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const u32x4 h0 = qx[(((hg * kKX + ks) * 2 + 0) * 2 + 0) * kWave + lane];
+        const u32x4 h1 = qx[(((hg * kKX + ks) * 2 + 0) * 2 + 1) * kWave + lane];
+        const u32x4 l0 = qx[(((hg * kKX + ks) * 2 + 1) * 2 + 0) * kWave + lane];
+        const u32x4 l1 = qx[(((hg * kKX + ks) * 2 + 1) * 2 + 1) * kWave + lane];
+        qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
+        qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
+      }
+      if constexpr (kRope > 0) {
+        const int src = (g & 1) * 16 + li;
+        const u32x4 t0 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 0) * kWave + src];
+        const u32x4 t1 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 1) * kWave + src];
+        qtail = i32x8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
+      }
+    }
+  }
+  };
+  if constexpr (kShareQ && kGroups != 4) {
     if (is_qk) {
       const u32x4* qx = (const u32x4*)(smem + kQxOff);
 #pragma unroll
@@ -829,7 +862,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   int vrow[2], vswz[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int slot = kBPW == 2 ? 32 * h + 16 * (g & 1) + 8 * (g >> 1) + (li >> 1)
+    const int slot = kBPW >= 2 ? 32 * h + 16 * (g & 1) + 8 * (g >> 1) + (li >> 1)
                                : 32 * h + 8 * g + (li >> 1);
     vrow[h] = slot * D + 8 * (li & 1);
     vswz[h] = tile_swizzle<D>(slot) << 4;
@@ -903,6 +936,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // i - 1. Each role keeps its own registers (the query terms, the
   // accumulators) inside its own branch.
   if (is_qk) {
+    if constexpr (kGroups == 4) load_qterms();
     const float pinf = opaque_inf();
     for (int pass = 0; pass < 2; ++pass) {
       l_part = 0.f;
@@ -924,7 +958,9 @@ void dsa_decode_kernel(DecodeArgs a) {
           // ---- S^T = K Q^T over this wave's two blocks, K operands
           // prefetched kKPre MFMA steps ahead
           f32x4 S[kBPW];
-          float mh = -INFINITY;  // max of this lane's weight block
+          float mh[kWB];  // max of this lane's weight block(s)
+#pragma unroll
+          for (int w = 0; w < kWB; ++w) mh[w] = -INFINITY;
           if (score) {
             const DSA_LDS uint8_t* kt = lds + k_off(it);
             constexpr int kSteps = kBPW * kKSteps;
@@ -989,7 +1025,7 @@ void dsa_decode_kernel(DecodeArgs a) {
                 for (int i = 0; i < 4; ++i)
                   if (token_of_slot(16 * (kBPW * part + k) + 4 * g + i) >= nvalid) S[k][i] = -INFINITY;
             }
-            {
+            if constexpr (kWB == 1) {
               // A weight block's 16 tokens: with two products per wave, this
               // lane's 8 (4 in each) and those of the lane 16 apart (one lane
               // swap); with one, the 4 of each lane group (two swaps). The
@@ -998,15 +1034,28 @@ void dsa_decode_kernel(DecodeArgs a) {
               float a = max2(max2(S[0][0], S[0][1], pinf), max2(S[0][2], S[0][3], pinf), pinf);
               if constexpr (kBPW == 2)
                 a = max2(a, max2(max2(S[1][0], S[1][1], pinf), max2(S[1][2], S[1][3], pinf), pinf), pinf);
-              mh = max_xor16(a, pinf);
-              if constexpr (kBPW == 1) mh = max_xor32(mh, pinf);
-              m_seen = max2(m_seen, mh, pinf);
+              mh[0] = max_xor16(a, pinf);
+              if constexpr (kBPW == 1) mh[0] = max_xor32(mh[0], pinf);
+              m_seen = max2(m_seen, mh[0], pinf);
+            } else {
+              // Four products: two weight blocks, each pairing products 2w and
+              // 2w + 1 as two products do.
+#pragma unroll
+              for (int w = 0; w < kWB; ++w) {
+                const int k0 = 2 * w;
+                const float a = max2(max2(max2(S[k0][0], S[k0][1], pinf), max2(S[k0][2], S[k0][3], pinf), pinf),
+                                     max2(max2(S[k0 + 1][0], S[k0 + 1][1], pinf),
+                                          max2(S[k0 + 1][2], S[k0 + 1][3], pinf), pinf), pinf);
+                mh[w] = max_xor16(a, pinf);
+                m_seen = max2(m_seen, mh[w], pinf);
+              }
             }
           }
           if (pass == 0 && it == 0) {
             // first tile: the reference is the tile's max over the group's
             // scoring waves
-            if (score) xch_f[wave][lane] = max_xor32(mh, pinf) * score_scale;  // score_scale > 0
+            if (score)  // score_scale > 0
+              xch_f[wave][lane] = max_xor32(kWB == 2 ? max2(mh[0], mh[kWB - 1], pinf) : mh[0], pinf) * score_scale;
             barrier_lds();
             if (ntiles > 0) {
               float m = -INFINITY;
@@ -1017,35 +1066,64 @@ void dsa_decode_kernel(DecodeArgs a) {
             }
           }
           if (score) {
-            // ---- weights, per 16-token block: the block's largest weight of
-            // the head maps to [128, 256) (a block with no valid token:
-            // exponent -100, weights 0)
-            const float x = fmaf(mh, score_scale, -(mb7 + 7.f));  // log2 domain, against the reference
-            overflow |= x >= kSlack;
-            const float ef = floorf(__builtin_amdgcn_fmed3f(x, -100.f, 100.f));
-            const float bsub = mb7 + ef;
-            const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
-            float psum = 0.f;
+            if constexpr (kWB == 1) {
+              // ---- weights, per 16-token block: the block's largest weight of
+              // the head maps to [128, 256) (a block with no valid token:
+              // exponent -100, weights 0)
+              const float x = fmaf(mh[0], score_scale, -(mb7 + 7.f));  // log2 domain, against the reference
+              overflow |= x >= kSlack;
+              const float ef = floorf(__builtin_amdgcn_fmed3f(x, -100.f, 100.f));
+              const float bsub = mb7 + ef;
+              const int eb = (int)ef + 120;  // E8M0 byte of 2^(e - 7)
+              float psum = 0.f;
 #pragma unroll
-            for (int k = 0; k < kBPW; ++k) {
-              float p[4];
+              for (int k = 0; k < kBPW; ++k) {
+                float p[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
-              psum += (p[0] + p[1]) + (p[2] + p[3]);
-              int phi, plo;
-              split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
-              // head li, word (g & 1) (hi) and 2 + (g & 1) (lo) of PV lane
-              // group 2*(g >> 1) + k, operand half part (two products), or
-              // of lane group 2*(part & 1) + (g >> 1), half part >> 1 (one)
-              int* dst = kBPW == 2 ? (int*)&xch_p[it & 1][hg][part][(2 * (g >> 1) + k) * 16 + li]
-                                   : (int*)&xch_p[it & 1][hg][part >> 1][(2 * (part & 1) + (g >> 1)) * 16 + li];
-              dst[g & 1] = phi;
-              dst[2 + (g & 1)] = plo;
+                for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[k][i], score_scale, -bsub));
+                psum += (p[0] + p[1]) + (p[2] + p[3]);
+                int phi, plo;
+                split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
+                // head li, word (g & 1) (hi) and 2 + (g & 1) (lo) of PV lane
+                // group 2*(g >> 1) + k, operand half part (two products), or
+                // of lane group 2*(part & 1) + (g >> 1), half part >> 1 (one)
+                int* dst = kBPW == 2 ? (int*)&xch_p[it & 1][hg][part][(2 * (g >> 1) + k) * 16 + li]
+                                     : (int*)&xch_p[it & 1][hg][part >> 1][(2 * (part & 1) + (g >> 1)) * 16 + li];
+                dst[g & 1] = phi;
+                dst[2 + (g & 1)] = plo;
+              }
+              l_part += psum * __uint_as_float((uint32_t)eb << 23);
+              // scale of weight block 2*part + (g >> 1), or part (the lanes
+              // that share the block write the same byte)
+              xch_e[it & 1][hg][kBPW == 2 ? 2 * part + (g >> 1) : part][li] = eb;
+            } else {
+              // Four products: weight blocks 2w + (g >> 1) from products 2w
+              // and 2w + 1, in operand half w, laid out as two products lay
+              // out their part's half.
+#pragma unroll
+              for (int w = 0; w < kWB; ++w) {
+                const float x = fmaf(mh[w], score_scale, -(mb7 + 7.f));
+                overflow |= x >= kSlack;
+                const float ef = floorf(__builtin_amdgcn_fmed3f(x, -100.f, 100.f));
+                const float bsub = mb7 + ef;
+                const int eb = (int)ef + 120;
+                float psum = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                  float p[4];
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(S[2 * w + kk][i], score_scale, -bsub));
+                  psum += (p[0] + p[1]) + (p[2] + p[3]);
+                  int phi, plo;
+                  split_fp8x4(p[0], p[1], p[2], p[3], phi, plo);
+                  int* dst = (int*)&xch_p[it & 1][hg][w][(2 * (g >> 1) + kk) * 16 + li];
+                  dst[g & 1] = phi;
+                  dst[2 + (g & 1)] = plo;
+                }
+                l_part += psum * __uint_as_float((uint32_t)eb << 23);
+                xch_e[it & 1][hg][2 * w + (g >> 1)][li] = eb;
+              }
             }
-            l_part += psum * __uint_as_float((uint32_t)eb << 23);
-            // scale of weight block 2*part + (g >> 1), or part (the lanes
-            // that share the block write the same byte)
-            xch_e[it & 1][hg][kBPW == 2 ? 2 * part + (g >> 1) : part][li] = eb;
           }
         }
       if (pass == 0 && !redo_needed(overflow)) break;
@@ -1080,20 +1158,36 @@ void dsa_decode_kernel(DecodeArgs a) {
           // blocks: one MFMA per head group and block (64 tokens, hi and lo
           // terms), V operands prefetched kVPre blocks ahead.
           const int pt = it - 1;
+          // With four head groups the accumulators leave no room to hold the
+          // lane's LDS addresses through the loop: they are recomputed each
+          // step from a laundered lane id.
+          int ln = lane, jb = jbase << 4;
+          if constexpr (kGroups == 4) asm volatile("" : "+v"(ln), "+v"(jb));
           i32x8 pB[kGroups];
           int psc[kGroups];
 #pragma unroll
           for (int x = 0; x < kGroups; ++x) {
-            const i32x4 h0 = xch_p[pt & 1][x][0][lane], h1 = xch_p[pt & 1][x][1][lane];
+            const int pl = kGroups == 4 ? ln : lane;
+            const i32x4 h0 = xch_p[pt & 1][x][0][pl], h1 = xch_p[pt & 1][x][1][pl];
             pB[x] = i32x8{h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-            psc[x] = xch_e[pt & 1][x][g][li];
+            psc[x] = kGroups == 4 ? xch_e[pt & 1][x][ln >> 4][ln & 15] : xch_e[pt & 1][x][g][li];
           }
           const DSA_LDS uint8_t* vt = lds + v_off(pt);
+          int vr[2] = {vrow[0], vrow[1]}, vs[2] = {vswz[0], vswz[1]};
+          if constexpr (kGroups == 4) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int slot = 32 * h + 16 * ((ln >> 4) & 1) + 8 * (ln >> 5) + ((ln & 15) >> 1);
+              vr[h] = slot * D + 8 * (ln & 1);
+              vs[h] = tile_swizzle<D>(slot) << 4;
+            }
+          }
           auto load_v = [&](int j0) -> i32x8 {
             i32x8 vop;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const int addr = (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
+              const int addr = kGroups == 4 ? ((jb + (j0 << 4)) ^ vs[u]) + vr[u]
+                                            : (((jbase + j0) << 4) ^ vswz[u]) + vrow[u];
               const i32x2 v2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DSA_LDS i32x2*)(vt + addr));
               vop[4 * u] = v2.x;      // against the hi terms
               vop[4 * u + 1] = v2.y;
@@ -1102,7 +1196,7 @@ void dsa_decode_kernel(DecodeArgs a) {
             }
             return vop;
           };
-          constexpr int kVPre = 2;
+          constexpr int kVPre = kGroups == 4 ? 1 : 2;
           i32x8 vbuf[kVPre + 1];
 #pragma unroll
           for (int j = 0; j < kVPre && j < kCB; ++j) vbuf[j] = load_v(j);
@@ -1234,6 +1328,8 @@ void dsa_decode_kernel(DecodeArgs a) {
     }
     return;
   }
+  // (the planner refuses the in-kernel merge for blocks of four head groups)
+  if constexpr (kGroups <= 2) {
   if (tid == 0) flag_sh = atomicAdd(arrived, 1) == a.chunks - 1 ? 2 : 0;
   __syncthreads();
   if (flag_sh != 2) {
@@ -1375,6 +1471,7 @@ void dsa_decode_kernel(DecodeArgs a) {
       *(bf16x4*)(orow + 16 * (src * kCB + unit_j(u)) + 4 * g) = v;
     }
   }
+  }  // kGroups <= 2
 }
 
 // Scratch of the entry point that allocates nothing (dsa_decode_launch_static):
@@ -1502,7 +1599,7 @@ hipError_t launch_g(bool split_v, bool rope, bool combine, dim3 grid, hipStream_
                     const DecodeArgs& args) {
   const dim3 block(waves_of(kGroups) * kWave);
   if (rope) {
-    if constexpr (D == 512)
+    if constexpr (D == 512 && kGroups <= 2)  // (the planner keeps rope tails to 32-head blocks)
       hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, false, 64>), grid, block, 0, st, args);
   } else if (split_v) {
     hipLaunchKernelGGL((dsa_decode_kernel<D, kGroups, true>), grid, block, 0, st, args);
@@ -1520,8 +1617,10 @@ hipError_t launch_g(bool split_v, bool rope, bool combine, dim3 grid, hipStream_
 template <int D>
 hipError_t launch_d(int groups, bool split_v, bool rope, bool combine, dim3 grid,
                     hipStream_t st, const DecodeArgs& args) {
-  return groups == 1 ? launch_g<D, 1>(split_v, rope, combine, grid, st, args)
-                     : launch_g<D, 2>(split_v, rope, combine, grid, st, args);
+  if (groups == 1) return launch_g<D, 1>(split_v, rope, combine, grid, st, args);
+  if (groups == 2) return launch_g<D, 2>(split_v, rope, combine, grid, st, args);
+  if constexpr (D == 512) return launch_g<D, 4>(split_v, rope, combine, grid, st, args);
+  return hipErrorInvalidValue;  // (64-head blocks are planned for kv_lora_rank 512 only)
 }
 
 

@@ -149,10 +149,21 @@ int validate_params(const dsa_decode_params* p, dsa_decode_params* norm) {
     m << "dsa_decode_plan: unknown flags 0x" << std::hex << p->flags;
     return fail(DSA_DECODE_ERR_INVALID, m.str());
   }
-  if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS16) {
+  if (p->layout < DSA_DECODE_LAYOUT_AUTO || p->layout > DSA_DECODE_LAYOUT_HEADS64) {
     m << "dsa_decode_plan: layout " << p->layout
-      << " is not 0 (auto), 1 (32-head blocks) or 2 (16-head blocks)";
+      << " is not 0 (auto), 1 (32-head blocks), 2 (16-head blocks) or 3 (64-head blocks)";
     return fail(DSA_DECODE_ERR_INVALID, m.str());
+  }
+  // 64-head blocks are compiled for the 512-wide latent alone; their LDS
+  // leaves no room for rope tails, and the in-kernel merge takes at most two
+  // head groups per workgroup.
+  if (p->layout == DSA_DECODE_LAYOUT_HEADS64 &&
+      (p->kv_lora_rank != 512 || p->qk_rope_dim != 0 ||
+       (p->flags & DSA_DECODE_FLAG_MERGE_IN_KERNEL))) {
+    m << "dsa_decode_plan: 64-head blocks (layout 3) need kv_lora_rank 512, no rope tail and "
+         "no DSA_DECODE_FLAG_MERGE_IN_KERNEL (got kv_lora_rank " << p->kv_lora_rank
+      << ", qk_rope_dim " << p->qk_rope_dim << ", flags 0x" << std::hex << p->flags << ")";
+    return fail(DSA_DECODE_ERR_UNSUPPORTED, m.str());
   }
   // Offsets into the selection, q and out are formed in 64-bit arithmetic
   // on the device; the per-row element counts must fit 32 bits.
@@ -170,15 +181,28 @@ void plan_layout(dsa_decode_plan_s* plan) {
   const int64_t R = p.num_rows, H = p.num_q_heads, D = p.kv_lora_rank,
                 W = p.sel_width;
   // Blocks of 32 heads (two 16-head groups, eight waves) unless the heads
-  // fit one group. Every workgroup holds a CU's LDS, so the grid aims at one
-  // workgroup per CU.
+  // fit one group, or 64-head blocks where they still give every CU a
+  // workgroup without splitting rows (many rows: one step over four head
+  // groups costs less than two steps over two) and are compiled (512-wide
+  // latent, no rope tail, no in-kernel merge). Every workgroup holds a CU's
+  // LDS, so the grid aims at one workgroup per CU.
   int layout = p.layout;
-  if (layout == DSA_DECODE_LAYOUT_AUTO)
-    layout = H <= kHeadsPerSmallBlock ? DSA_DECODE_LAYOUT_HEADS16 : DSA_DECODE_LAYOUT_HEADS32;
-  plan->layout = layout;
-  plan->heads_per_block =
-      layout == DSA_DECODE_LAYOUT_HEADS16 ? kHeadsPerSmallBlock : kHeadsPerBlock;
   const int64_t wg_target = plan->num_cus;
+  if (layout == DSA_DECODE_LAYOUT_AUTO) {
+    const bool h64_ok = D == 512 && p.qk_rope_dim == 0 &&
+                        !(p.flags & DSA_DECODE_FLAG_MERGE_IN_KERNEL);
+    if (H <= kHeadsPerSmallBlock)
+      layout = DSA_DECODE_LAYOUT_HEADS16;
+    else if (h64_ok && H > kHeadsPerBlock &&
+             R * ((H + kHeadsPerLargeBlock - 1) / kHeadsPerLargeBlock) >= wg_target)
+      layout = DSA_DECODE_LAYOUT_HEADS64;
+    else
+      layout = DSA_DECODE_LAYOUT_HEADS32;
+  }
+  plan->layout = layout;
+  plan->heads_per_block = layout == DSA_DECODE_LAYOUT_HEADS16   ? kHeadsPerSmallBlock
+                           : layout == DSA_DECODE_LAYOUT_HEADS64 ? kHeadsPerLargeBlock
+                                                                 : kHeadsPerBlock;
   plan->head_blocks = (int)((H + plan->heads_per_block - 1) / plan->heads_per_block);
   // A row can attend at most min(W, max_seq_len) distinct tokens.
   const int64_t wmax = std::min<int64_t>(W, p.max_seq_len);

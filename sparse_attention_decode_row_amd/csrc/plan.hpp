@@ -31,6 +31,7 @@ inline uint64_t token_bytes(const dsa_decode_params& p) {
 // or a single group.
 constexpr int kHeadsPerBlock = 32;
 constexpr int kHeadsPerSmallBlock = 16;
+constexpr int kHeadsPerLargeBlock = 64;  // four 16-head groups (kv_lora_rank 512, no rope tail)
 // Workspace sub-buffer alignment.
 constexpr size_t kWsAlign = 256;
 

@@ -78,6 +78,9 @@ def plan(native, **kw):
     (dict(chunk_tokens=4096), -1, "chunk_tokens"),
     (dict(rows_per_sequence=-1), -1, "rows_per_sequence"),
     (dict(num_rows=10, rows_per_sequence=4), -1, "divides num_rows 10"),
+    (dict(layout=3, kv_lora_rank=256), -2, "64-head blocks"),
+    (dict(layout=3, qk_rope_dim=64), -2, "64-head blocks"),
+    (dict(layout=3, flags=2), -2, "64-head blocks"),
 ])
 def test_plan_rejects(native, kw, status, needle):
     with pytest.raises(native.DsaDecodeError) as e:
@@ -161,8 +164,11 @@ def test_split_plan(native, kw, chunks, ct):
     assert info["workgroups"] == (rows + 7) // 8 * 8 * chunks * info["head_blocks"]
     heads = kw.get("num_q_heads", 64)
     small = kw.get("layout", 0) == 2 or heads <= 16
-    assert info["layout"] == (2 if small else 1)
-    assert info["heads_per_block"] == (16 if small else 32)
+    # 64-head blocks when one block per row still fills the 256 CUs
+    large = (not small and kw.get("layout", 0) == 0 and heads > 32
+             and kw.get("kv_lora_rank", 512) == 512 and rows * -(-heads // 64) >= 256)
+    assert info["layout"] == (2 if small else 3 if large else 1)
+    assert info["heads_per_block"] == (16 if small else 64 if large else 32)
     assert info["head_blocks"] == (heads + info["heads_per_block"] - 1) // info["heads_per_block"]
     assert info["device"] == -1
 
@@ -176,8 +182,12 @@ def test_layouts(native):
     assert plan(native).info()["layout"] == 1
     assert plan(native, num_q_heads=16).info()["layout"] == 2
     assert plan(native, num_q_heads=17).info()["layout"] == 1
+    # 64-head blocks: one block per row, the rows split in two to fill the chip
+    h64 = plan(native, layout=3).info()
+    assert (h64["heads_per_block"], h64["head_blocks"], h64["layout"]) == (64, 1, 3)
+    assert (h64["chunks_per_row"], h64["workgroups"]) == (2, 256)
     with pytest.raises(native.DsaDecodeError) as e:
-        plan(native, layout=3)
+        plan(native, layout=4)
     assert e.value.status == native.DSA_DECODE_ERR_INVALID
 
 
@@ -380,10 +390,12 @@ def test_planner_invariants_over_random_geometries(native):
     @given(rows=st.integers(1, 300), heads=st.integers(1, 200),
            D=st.sampled_from([64, 128, 256, 512]), B=st.sampled_from([4, 16, 64]),
            width=st.integers(1, 5000), L=st.integers(1, 300000),
-           ct=st.integers(0, 32), layout=st.integers(0, 2), k=st.integers(0, 6))
+           ct=st.integers(0, 32), layout=st.integers(0, 3), k=st.integers(0, 6))
     def check(rows, heads, D, B, width, L, ct, layout, k):
         if k > 1 and rows % k:
             k = 1
+        if layout == 3 and D != 512:
+            layout = 0  # 64-head blocks are compiled for the 512-wide latent
         stride = -(-L // B)
         p = native.Plan(device=-1, num_rows=rows, num_q_heads=heads, kv_lora_rank=D,
                         block_size=B, index_kpool=4 if B % 4 == 0 else 1, sel_width=width,
@@ -398,7 +410,11 @@ def test_planner_invariants_over_random_geometries(native):
         assert T + lead <= 2048                      # chunk 0's row table fits
         assert (C - 1) * T + lead < max(wmax, 1) or C == 1   # no chunk is always empty
         assert HB == -(-heads // info["heads_per_block"])
-        assert info["heads_per_block"] == (16 if info["layout"] == 2 else 32)
+        assert info["heads_per_block"] == {1: 32, 2: 16, 3: 64}[info["layout"]]
+        if layout:
+            assert info["layout"] == layout
+        elif info["layout"] == 3:  # chosen only where one block per row fills the chip
+            assert D == 512 and heads > 32 and rows * -(-heads // 64) >= info["num_cus"]
         assert info["merges_chunks"] == (C > 1)
         units = rows * C
         # the rows_per_sequence x chunks units of a sequence (one row when

@@ -189,10 +189,11 @@ def test_random_shapes(H, case):
     assert err.max() <= H.TOL
 
 
-@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("layout", [1, 2, 3])
 def test_both_layouts_match_the_oracle(H, layout):
-    """32-head blocks (eight waves) and 16-head blocks (four waves) compute
-    the same decode; run each on a split, multi-block shape."""
+    """32-head, 16-head and 64-head blocks (eight waves each) compute the
+    same decode; run each on a split, multi-block shape (96 heads: a partial
+    last block in every layout)."""
     rng = np.random.default_rng(40 + layout)
     wl = WL.random_case(rng, rows=5, heads=96, D=512, block_size=64, max_len=4000,
                         width=1800)
@@ -205,6 +206,38 @@ def test_both_layouts_match_the_oracle(H, layout):
         err = H.normwise_err(run.out, want)
         print(f"layout {layout} chunk {ct}: plan {run.info} max err {err.max():.3e}")
         assert err.max() <= H.TOL
+
+
+# 64-head blocks: one scoring wave per 16-head group scores the whole tile
+CASES64 = [
+    # (seed, rows, heads, B, max_len, width, chunk_tokens, split_v)
+    (0, 3, 64, 64, 5000, 2048, 0, False),
+    (1, 4, 96, 64, 3000, 1500, 192, False),
+    (2, 2, 48, 16, 900, 1000, 64, True),
+    (3, 5, 128, 32, 2600, 2100, 512, False),
+    (4, 2, 17, 64, 700, 600, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES64, ids=[f"h64_{c[0]}" for c in CASES64])
+def test_64_head_blocks(H, case):
+    seed, rows, heads, B, max_len, width, ct, split_v = case
+    rng = np.random.default_rng(900 + seed)
+    wl = WL.random_case(rng, rows=rows, heads=heads, D=512, block_size=B,
+                        max_len=max_len, width=width)
+    _announce("heads64", seed=seed, rows=rows, heads=heads, W=width, chunk=ct,
+              split_v=split_v)
+    v_host = v_dev = None
+    if split_v:
+        v_host = WL.host_pool(rng, wl.num_pages, B, 512, 1.0, wl.k_scale)
+        v_dev = H.u8(v_host)
+    run = H.run_gpu(wl, v_pool=v_dev, chunk_tokens=ct, layout=3)
+    assert run.info["layout"] == 3 and run.info["heads_per_block"] == 64
+    H.check_selection(wl, run)
+    want = H.oracle_rows(wl, range(rows), host_v_pool=v_host)
+    err = H.normwise_err(run.out, want)
+    print(f"h64 case {seed}: plan {run.info} max err {err.max():.3e}")
+    assert err.max() <= H.TOL
 
 
 def test_split_invariance(H):
