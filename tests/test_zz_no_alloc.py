@@ -3,8 +3,9 @@ for callers that cannot allocate device memory: it runs the same kernels as
 dsa_decode_launch with the library's static scratch in place of a caller
 workspace. Checked through the C ABI against dsa_decode_launch on two calls
 in a row, the second with a smaller input (the scratch then holds what the
-first call left), both split into several chunks per row so that the arrival
-counters and the partials are used; and against the oracle."""
+first call left), then a third in 64-head blocks, all split into several
+chunks per row so that the arrival counters and the partials are used; and
+against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -44,8 +45,12 @@ def test_static_scratch_matches_the_workspace_entry_point(H):
                          width=2048)
     small = WL.random_case(rng, rows=5, heads=24, D=256, block_size=32, max_len=3000,
                            width=900)
+    wide = WL.random_case(rng, rows=4, heads=80, D=512, block_size=64, max_len=4000,
+                          width=1500)
     for name, wl, kw in (("first, split into chunks", big, {}),
-                         ("second, smaller, 128-token chunks", small, {"chunk_tokens": 128})):
+                         ("second, smaller, 128-token chunks", small, {"chunk_tokens": 128}),
+                         ("third, 64-head blocks, 256-token chunks", wide,
+                          {"layout": 3, "chunk_tokens": 256})):
         print(f"\n[gpu case] launch_static {name}: rows {wl.rows} heads {wl.heads} "
               f"D {wl.D}", flush=True)
         out_s, out_w, info = _both(H, wl, **kw)
