@@ -780,8 +780,7 @@ void dsa_decode_kernel(DecodeArgs a) {
   // Otherwise they are read here (the same reads written out below: wrapped
   // in this lambda the compiler builds their addresses differently).
   auto load_qterms = [&]() {
-  if constexpr (kShareQ) {
-    {
+    if constexpr (kShareQ) {
       const u32x4* qx = (const u32x4*)(smem + kQxOff);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
@@ -792,14 +791,8 @@ void dsa_decode_kernel(DecodeArgs a) {
         qhi[ks] = i32x8{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
         qlo[ks] = i32x8{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
       }
-      if constexpr (kRope > 0) {
-        const int src = (g & 1) * 16 + li;
-        const u32x4 t0 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 0) * kWave + src];
-        const u32x4 t1 = qx[(((hg * kKX + kKSteps) * 2 + (g >> 1)) * 2 + 1) * kWave + src];
-        qtail = i32x8{(int)t0.x, (int)t0.y, (int)t0.z, (int)t0.w, (int)t1.x, (int)t1.y, (int)t1.z, (int)t1.w};
-      }
+      // (64-head blocks carry no rope tail)
     }
-  }
   };
   if constexpr (kShareQ && kGroups != 4) {
     if (is_qk) {
@@ -844,7 +837,8 @@ void dsa_decode_kernel(DecodeArgs a) {
   // tokens of a head share one exponent. In lane group G, bytes 16*h ..
   // 16*h + 7 hold the hi terms of 8 slots and bytes 16*h + 8 .. +15 their lo
   // terms:
-  // - two blocks per scoring wave: slots 32*h + 16*(G & 1) + 8*(G >> 1) ..
+  // - two blocks per scoring wave (four: each pair as the two of one part,
+  //   pair h in operand half h): slots 32*h + 16*(G & 1) + 8*(G >> 1) ..
   //   +7. Block 2*h + (G >> 1) thus holds the 8 slots that scoring lane
   //   group g of wave part h holds in each of its two products, for
   //   g = 2*(G >> 1) and g + 1: a lane and the lane 16 apart. Slot 32*h +
@@ -955,7 +949,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           if (dma_wave) dma_rows(it, drow);
           if (!kSplitV) tail_dma(it + 2);
 
-          // ---- S^T = K Q^T over this wave's two blocks, K operands
+          // ---- S^T = K Q^T over this wave's blocks, K operands
           // prefetched kKPre MFMA steps ahead
           f32x4 S[kBPW];
           float mh[kWB];  // max of this lane's weight block(s)
