@@ -689,24 +689,33 @@ void dsa_decode_kernel(DecodeArgs a) {
   };
   // Tile it has landed for this wave once only the DMAs of the next tile
   // (issued in the previous step) may still be outstanding.
+  // (At step 0 only tile 0 is out, so step 0 waits for every load.)
   auto wait_tile = [&](int it) {
-    if (kSplitV || it + 1 >= ntiles) wait_vmcnt<0>();
+    if (kSplitV || it + 1 >= ntiles || it == 0) wait_vmcnt<0>();
     else if (kRope && wave < kTailInstr) wait_vmcnt<kInstr + 1>();
     else wait_vmcnt<kInstr>();
   };
-  // The first tiles (tile 0; with K and V the same bytes also tile 1) go out
-  // now; a separate V buffer is filled in the loop after every wave has read
-  // its query terms out of it.
+  // Tile 0 goes out now, and tile 1 (K and V the same bytes) at the start of
+  // step 0, once tile 0 has landed: every workgroup issues its first loads
+  // (ids, block-table rows, query rows) and its first tile together, and tile
+  // 0 lands sooner when that launch-wide burst does not also carry every
+  // workgroup's second tile (8 MiB fewer on the long-context shape). A
+  // separate V buffer is filled in the loop after every wave has read its
+  // query terms out of it.
   auto issue_first = [&]() {
     if (dma_wave) {
       if (ntiles > 0) issue_tile(0, k_off(0), a.k_cache);
       tail_dma(0);
-      if (!kSplitV && ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
+    }
+  };
+  auto issue_second = [&]() {  // step 0, after its barrier
+    if (!kSplitV && dma_wave) {
+      if (ntiles > 1) issue_tile(1, k_off(1), a.k_cache);
       tail_dma(1);
     }
   };
 
-  // The first tiles load while the query terms are prepared (issued after
+  // Tile 0 loads while the query terms are prepared (issued after
   // the query registers were first read, so that no wait for the query
   // loads can also wait for these).
   issue_first();
@@ -942,6 +951,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           // every read of the weights of it - 2 is done
           wait_tile(it);
           barrier_lds();
+          if (it == 0) issue_second();
           const bool score = it < ntiles;
           uint32_t drow[kNd];
           uint32_t c0 = dma_c0;
@@ -1135,6 +1145,7 @@ void dsa_decode_kernel(DecodeArgs a) {
           // every read of tile it - 2's buffer done).
           wait_tile(it);
           barrier_lds();
+          if (it == 0) issue_second();
           if (pass == 0 && it == 0) barrier_lds();  // the scoring waves' reference exchange
 
           uint32_t drow[kNd];
