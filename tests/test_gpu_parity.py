@@ -594,29 +594,35 @@ def test_plan_on_gfx950_device(H):
     assert props.gcnArchName.startswith("gfx950")
 
 
-def test_score_far_above_the_first_tiles_max(H):
-    """A late token whose score exceeds every earlier one by hundreds of
-    log2 units: the weights must stay finite and the result match the
-    oracle (the softmax is then essentially one-hot on that token)."""
-    D, B, L = 512, 64, 1024
+@pytest.mark.parametrize("layout", [2, 1, 3])
+def test_score_far_above_the_first_tiles_max(H, layout):
+    """Late tokens whose scores exceed every earlier one by hundreds of
+    log2 units, twice (a token at position 500, then a larger one at 900,
+    in different 16-token blocks of their tiles): the weights must stay
+    finite and the result match the oracle (the softmax is then essentially
+    one-hot on the last of them). Every head-block layout, whole rows and
+    rows split into chunks."""
+    D, B, L, heads = 512, 64, 1024, 64
     rng = np.random.default_rng(15)
     pages = L // B
     bt = rng.permutation(pages).astype(np.int32)[None, :]
     pool = WL.fp8_codes_from_f32(rng.standard_normal(pages * B * D, dtype=np.float32) * 0.5)
-    big = 900
-    base = (bt[0, big // B] * B + big % B) * D
-    pool[base:base + D] = 0x7E           # 448 in every column
-    q = np.zeros((1, 16, D), np.float32)
+    for pos, code in ((500, 0x7D), (900, 0x7E)):   # 416, then 448, in every column
+        base = (bt[0, pos // B] * B + pos % B) * D
+        pool[base:base + D] = code
+    q = np.zeros((1, heads, D), np.float32)
     q[0, :, :] = 8.0                      # large |q|: scores spread far
-    wl = WL.Workload(name="spread", rows=1, heads=16, D=D, block_size=B, kpool=4,
+    q[0, 1::2, :] = 6.0                   # heads differ in how far
+    wl = WL.Workload(name="spread", rows=1, heads=heads, D=D, block_size=B, kpool=4,
                      width=L, bt_stride=pages, cache_stride_bytes=B * D, max_seq_len=L,
                      num_pages=pages, sm_scale=1 / 16, k_scale=0.02, v_scale=0.02,
                      sigma=1.0, seed=0, q_bits=WL.bf16_bits_from_f32(q),
                      block_tables=bt, seq_lens=np.array([L], np.int32),
                      sel=np.arange(L, dtype=np.int32)[None, :], pool=pool)
+    want = H.oracle_rows(wl, [0])
     for ct in (0, 256):
-        _announce("score spread", chunk=ct)
-        run = H.run_gpu(wl, chunk_tokens=ct)
-        want = H.oracle_rows(wl, [0])
+        _announce("score spread", layout=layout, chunk=ct)
+        run = H.run_gpu(wl, chunk_tokens=ct, layout=layout)
+        assert run.info["layout"] == layout
         assert np.isfinite(run.out).all()
         assert H.normwise_err(run.out, want).max() <= H.TOL
