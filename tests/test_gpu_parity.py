@@ -258,11 +258,13 @@ def test_split_invariance(H):
 
 # ------------------------------------------------------------ special cases
 
-def test_single_token_is_exact_dequantised_row(H):
+@pytest.mark.parametrize("layout", [2, 1, 3])
+def test_single_token_is_exact_dequantised_row(H, layout):
     """One selected token (repeated, among holes): the output of every head
     is bf16(v_scale * dec(code)) bit for bit. The latent row holds all 254
-    finite codes, so this also checks the FP8 decode exhaustively."""
-    D, B = 512, 64
+    finite codes, so this also checks the FP8 decode exhaustively. Every
+    head-block layout."""
+    D, B, heads = 512, 64, 64
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
     row = np.resize(codes, D)   # 254 codes, repeated to fill the row
     pool = np.zeros(4 * B * D, np.uint8)
@@ -277,25 +279,27 @@ def test_single_token_is_exact_dequantised_row(H):
         pool[base:base + D] = row
         sel[r, ::4] = t[r]
     for vs in (1.0, 0.02):
-        wl = WL.Workload(name="single", rows=2, heads=16, D=D, block_size=B, kpool=4,
+        wl = WL.Workload(name="single", rows=2, heads=heads, D=D, block_size=B, kpool=4,
                          width=16, bt_stride=2, cache_stride_bytes=B * D,
                          max_seq_len=128, num_pages=4, sm_scale=1 / 16, k_scale=0.02,
                          v_scale=vs, sigma=1.0, seed=0,
-                         q_bits=WL.bf16_bits_from_f32(rng.standard_normal((2, 16, D), dtype=np.float32)),
+                         q_bits=WL.bf16_bits_from_f32(rng.standard_normal((2, heads, D), dtype=np.float32)),
                          block_tables=bt, seq_lens=seq_lens, sel=sel, pool=pool)
-        _announce("single token", v_scale=vs)
-        run = H.run_gpu(wl)
+        _announce("single token", v_scale=vs, layout=layout)
+        run = H.run_gpu(wl, layout=layout)
+        assert run.info["layout"] == layout
         dec = torch.from_numpy(row.copy()).view(torch.float8_e4m3fn).float()
         # the output is a weighted sum that starts from +0, so the -0 code
         # comes out as +0 (IEEE: +0 + -0 = +0); the oracle does the same
         want = (dec * torch.tensor(vs, dtype=torch.float32) + 0.0).to(torch.bfloat16)
         want_bits = want.view(torch.int16).numpy().view(np.uint16)
         for r in range(2):
-            for h in range(16):
+            for h in range(heads):
                 assert np.array_equal(run.out_bits[r, h], want_bits), (vs, r, h)
 
 
-def test_empty_selection_rows_are_zero(H):
+@pytest.mark.parametrize("layout", [2, 1, 3])
+def test_empty_selection_rows_are_zero(H, layout):
     rng = np.random.default_rng(10)
     wl = WL.random_case(rng, rows=4, heads=64, D=512, block_size=64, max_len=500,
                         width=300)
@@ -305,8 +309,8 @@ def test_empty_selection_rows_are_zero(H):
     sel[1] = seq_lens[1] + np.arange(300)    # all past the end
     seq_lens[2] = 0                          # nothing valid
     for ct in (0, 64):
-        _announce("empty rows", chunk=ct)
-        run = H.run_gpu(wl, sel=sel, seq_lens=seq_lens, chunk_tokens=ct)
+        _announce("empty rows", chunk=ct, layout=layout)
+        run = H.run_gpu(wl, sel=sel, seq_lens=seq_lens, chunk_tokens=ct, layout=layout)
         H.check_selection(wl, run, sel=sel, seq_lens=seq_lens)
         assert np.array_equal(run.out_bits[:3], np.zeros_like(run.out_bits[:3]))
         want = H.oracle_rows(wl, [3], sel=sel, seq_lens=seq_lens)
@@ -335,7 +339,8 @@ def test_repeats_holes_and_order_do_not_change_the_result(H):
     assert np.array_equal(noisy.out_bits, base.out_bits)
 
 
-def test_uniform_softmax_membership_probe(H):
+@pytest.mark.parametrize("layout", [2, 1, 3])
+def test_uniform_softmax_membership_probe(H, layout):
     """q = 0 makes every selected token weigh 1/n. With one-hot V rows
     (token t's latent row is e_t with FP8 1.0, v_scale 1) the output is
     nonzero exactly on the selected set, every nonzero equal to bf16(1/n):
@@ -349,18 +354,19 @@ def test_uniform_softmax_membership_probe(H):
         base = (bt[0, t // B] * B + t % B) * D
         pool[base + t] = 0x38   # 1.0
     sel = rng.integers(-3, L + 30, size=(1, 900)).astype(np.int32)
-    wl = WL.Workload(name="probe", rows=1, heads=16, D=D, block_size=B, kpool=4,
+    heads = 64
+    wl = WL.Workload(name="probe", rows=1, heads=heads, D=D, block_size=B, kpool=4,
                      width=900, bt_stride=pages, cache_stride_bytes=B * D,
                      max_seq_len=L, num_pages=pages, sm_scale=1.0, k_scale=1.0,
                      v_scale=1.0, sigma=1.0, seed=0,
-                     q_bits=np.zeros((1, 16, D), np.uint16), block_tables=bt,
+                     q_bits=np.zeros((1, heads, D), np.uint16), block_tables=bt,
                      seq_lens=np.array([L], np.int32), sel=sel, pool=pool)
     for ct in (0, 64):
-        _announce("membership probe", chunk=ct)
-        run = H.run_gpu(wl, chunk_tokens=ct)
+        _announce("membership probe", chunk=ct, layout=layout)
+        run = H.run_gpu(wl, chunk_tokens=ct, layout=layout)
         S = sorted({int(t) for t in sel[0] if 0 <= t < L})
         inv_n = torch.tensor(1.0 / len(S), dtype=torch.float32).to(torch.bfloat16).float().item()
-        for h in range(16):
+        for h in range(heads):
             nz = np.flatnonzero(run.out[0, h])
             assert nz.tolist() == S
             np.testing.assert_allclose(run.out[0, h, S], inv_n, rtol=2 ** -7)
