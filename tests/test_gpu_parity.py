@@ -165,6 +165,8 @@ CASES = [
     (10, 3, 64, 64, 16, 1200, 900, 64, False, False),
     (11, 2, 40, 256, 32, 3000, 2000, 0, False, True),
     (12, 2, 96, 128, 32, 1500, 1400, 128, True, False),
+    (13, 2, 64, 512, 64, 20000, 8192, 0, False, False),   # the planner's split: 64 chunks a row
+    (14, 2, 64, 512, 64, 20000, 8192, 2048, False, False),  # four chunks of the largest size
 ]
 
 
