@@ -167,6 +167,11 @@ CASES = [
     (12, 2, 96, 128, 32, 1500, 1400, 128, True, False),
     (13, 2, 64, 512, 64, 20000, 8192, 0, False, False),   # the planner's split: 64 chunks a row
     (14, 2, 64, 512, 64, 20000, 8192, 2048, False, False),  # four chunks of the largest size
+    # page sizes that are not a power of two (the translation divides), and larger pages
+    (15, 3, 64, 512, 12, 1500, 1200, 0, False, False),
+    (16, 2, 32, 256, 48, 3000, 2000, 256, True, False),
+    (17, 3, 64, 512, 128, 5000, 2048, 0, False, False),
+    (18, 2, 16, 512, 256, 9000, 2048, 512, False, True),
 ]
 
 
@@ -189,6 +194,10 @@ def test_random_shapes(H, case):
     err = H.normwise_err(run.out, want)
     print(f"case {seed}: plan {run.info} max err {err.max():.3e}")
     assert err.max() <= H.TOL
+    # without the selection export (the production path: every head block
+    # translates through its own branch-free placement when it can)
+    plain = H.run_gpu(wl, v_pool=v_dev, chunk_tokens=ct, with_selection=False)
+    assert np.array_equal(plain.out_bits, run.out_bits)
 
 
 @pytest.mark.parametrize("layout", [1, 2, 3])
