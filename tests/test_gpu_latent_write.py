@@ -93,7 +93,7 @@ def _run_case(H, rng, *, rows, D, B, pages, stride_pad, sigma, inv, eps=1e-6, ne
 
 
 @pytest.mark.parametrize("D,B,pad", [(512, 64, 0), (512, 16, 256), (256, 32, 0),
-                                     (128, 64, 128), (64, 16, 0)])
+                                     (128, 64, 128), (64, 16, 0), (512, 48, 0), (256, 12, 64)])
 def test_writer_matches_oracle(H, D, B, pad):
     rng = np.random.default_rng(100 + D + B)
     _announce("latent_write", D=D, B=B, pad=pad)

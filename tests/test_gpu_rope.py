@@ -46,23 +46,25 @@ def test_glm_shaped_with_rope_tail(H, in_kernel):
     assert err.max() <= H.TOL
 
 
-@pytest.mark.parametrize("seed,heads,layout,ct,shared", [
-    (1, 16, 0, 0, False),
-    (2, 40, 1, 0, False),
-    (3, 64, 2, 256, False),
-    (4, 24, 1, 64, True),
-    (5, 128, 0, 1024, False),
-    (6, 32, 1, 2048, False),   # one workgroup takes 2048 tokens: the tail ring wraps ten times
-    (7, 16, 2, 2048, True),
+@pytest.mark.parametrize("seed,heads,layout,ct,shared,B", [
+    (1, 16, 0, 0, False, 64),
+    (2, 40, 1, 0, False, 64),
+    (3, 64, 2, 256, False, 64),
+    (4, 24, 1, 64, True, 64),
+    (5, 128, 0, 1024, False, 64),
+    (6, 32, 1, 2048, False, 64),   # one workgroup takes 2048 tokens: the tail ring wraps ten times
+    (7, 16, 2, 2048, True, 64),
+    (8, 64, 0, 0, False, 12),      # pages of 12 and 128 tokens of 576 bytes
+    (9, 32, 1, 128, True, 128),
 ])
-def test_random_shapes_with_rope_tail(H, seed, heads, layout, ct, shared):
+def test_random_shapes_with_rope_tail(H, seed, heads, layout, ct, shared, B):
     rng = np.random.default_rng(900 + seed)
     wide = ct == 2048
-    base = WL.random_case(rng, rows=5, heads=heads, D=512, block_size=64,
+    base = WL.random_case(rng, rows=5, heads=heads, D=512, block_size=B,
                           max_len=6000 if wide else 3000, width=2048 if wide else 1500,
                           shared_table=shared)
     wl = WL.with_rope_tail(base, seed=seed)
-    _announce("rope random", seed=seed, heads=heads, layout=layout, ct=ct, shared=shared)
+    _announce("rope random", seed=seed, heads=heads, layout=layout, ct=ct, shared=shared, B=B)
     run = H.run_gpu(wl, chunk_tokens=ct, layout=layout)
     H.check_selection(wl, run)
     want = H.oracle_rows(wl, range(wl.rows))
