@@ -328,6 +328,26 @@ def test_empty_selection_rows_are_zero(H, layout):
         assert H.normwise_err(run.out[3:4], want).max() <= H.TOL
 
 
+def test_seq_lens_are_clamped_to_0_and_max_seq_len(H):
+    """A negative seq_lens[r] attends nothing and one above max_seq_len
+    attends as if it were max_seq_len (the launch contract: ids are kept
+    when 0 <= t < min(max(seq_len, 0), max_seq_len))."""
+    rng = np.random.default_rng(16)
+    wl = WL.random_case(rng, rows=4, heads=32, D=512, block_size=64, max_len=1000,
+                        width=900)
+    sel = wl.sel.copy()
+    sel[1, :300] = np.arange(700, 1600, 3)     # ids on both sides of max_seq_len
+    given = np.array([-5, 1500, 1000, 37], np.int32)
+    clamped = np.clip(given, 0, wl.max_seq_len).astype(np.int32)
+    for ct in (0, 128):
+        _announce("clamped seq_lens", chunk=ct)
+        run = H.run_gpu(wl, sel=sel, seq_lens=given, chunk_tokens=ct)
+        H.check_selection(wl, run, sel=sel, seq_lens=clamped)
+        assert np.array_equal(run.out_bits[0], np.zeros_like(run.out_bits[0]))
+        want = H.oracle_rows(wl, [1, 2, 3], sel=sel, seq_lens=clamped)
+        assert H.normwise_err(run.out[1:], want).max() <= H.TOL
+
+
 def test_repeats_holes_and_order_do_not_change_the_result(H):
     """The selection is normalised to a sorted set before the attention, so
     the output is bit-identical whatever the repeats, holes and order."""
