@@ -348,6 +348,24 @@ def test_seq_lens_are_clamped_to_0_and_max_seq_len(H):
         assert H.normwise_err(run.out[1:], want).max() <= H.TOL
 
 
+@pytest.mark.parametrize("k_scale,v_scale", [(1e-6, 1e-20), (0.5, 1e4), (0.05, -3.0)])
+def test_extreme_and_negative_scales(H, k_scale, v_scale):
+    """Dequantisation scales far from the pool's own: k_scale 1e-6 flattens
+    the softmax to uniform, 0.5 sharpens it; v_scale 1e-20 and 1e4 scale the
+    output far from 1 (bf16 keeps fp32's exponent range), and a negative
+    v_scale flips its sign. Whole rows and rows split into chunks."""
+    rng = np.random.default_rng(17)
+    base = WL.random_case(rng, rows=3, heads=64, D=512, block_size=64, max_len=2500,
+                          width=1200)
+    wl = WL.Workload(**{**base.__dict__, "k_scale": k_scale, "v_scale": v_scale})
+    want = H.oracle_rows(wl, range(wl.rows))
+    for ct in (0, 256):
+        _announce("scales", k_scale=k_scale, v_scale=v_scale, chunk=ct)
+        run = H.run_gpu(wl, chunk_tokens=ct, with_selection=False)
+        assert np.isfinite(run.out).all()
+        assert H.normwise_err(run.out, want).max() <= H.TOL
+
+
 def test_repeats_holes_and_order_do_not_change_the_result(H):
     """The selection is normalised to a sorted set before the attention, so
     the output is bit-identical whatever the repeats, holes and order."""
