@@ -113,18 +113,21 @@ def test_verify_rows_co_scheduled_per_sequence(H):
     assert err.max() <= H.TOL
 
 
-@pytest.mark.parametrize("k,chunk_tokens,heads", [(3, 64, 40), (5, 0, 40), (2, 64, 16), (4, 0, 12)])
-def test_co_scheduled_rows_with_padding_and_splits(H, k, chunk_tokens, heads):
+@pytest.mark.parametrize("k,chunk_tokens,heads,D,layout", [
+    (3, 64, 40, 128, 0), (5, 0, 40, 128, 0), (2, 64, 16, 128, 0), (4, 0, 12, 128, 0),
+    (3, 64, 80, 512, 3), (4, 0, 64, 512, 3)])
+def test_co_scheduled_rows_with_padding_and_splits(H, k, chunk_tokens, heads, D, layout):
     """A sequence count that leaves a block of 8 partly empty, with and
-    without split chunks, in 32-head and 16-head blocks: same bits as
+    without split chunks, in 16-, 32- and 64-head blocks: same bits as
     independent scheduling, oracle parity on every row."""
     rng = np.random.default_rng(77 + k)
     seqs = 5
-    wl = WL.random_case(rng, rows=seqs * k, heads=heads, D=128, block_size=16,
+    wl = WL.random_case(rng, rows=seqs * k, heads=heads, D=D, block_size=16,
                         width=300, max_len=900)
-    _announce("co-scheduled", rows=wl.rows, k=k, chunk_tokens=chunk_tokens)
-    base = H.run_gpu(wl, chunk_tokens=chunk_tokens)
-    run = H.run_gpu(wl, chunk_tokens=chunk_tokens, rows_per_sequence=k)
+    _announce("co-scheduled", rows=wl.rows, k=k, chunk_tokens=chunk_tokens, heads=heads,
+              layout=layout)
+    base = H.run_gpu(wl, chunk_tokens=chunk_tokens, layout=layout)
+    run = H.run_gpu(wl, chunk_tokens=chunk_tokens, rows_per_sequence=k, layout=layout)
     H.check_selection(wl, run)
     assert np.array_equal(run.out_bits, base.out_bits)
     want = H.oracle_rows(wl, range(wl.rows))
