@@ -502,8 +502,8 @@ def test_deterministic(H):
     assert np.array_equal(a.out_bits, b.out_bits)
 
 
-@pytest.mark.parametrize("in_kernel", [False, True])
-@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("layout,in_kernel", [(1, False), (1, True), (2, False), (2, True),
+                                              (3, False)])   # 64-head blocks: combine kernel only
 def test_many_chunk_merges_repeated_on_one_workspace(H, layout, in_kernel):
     """The split merge under load: 64-token chunks (up to 32 per row), 30
     launches on one workspace without re-initialising it, merged by the
