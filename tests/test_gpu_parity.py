@@ -254,15 +254,18 @@ def test_64_head_blocks(H, case):
     assert err.max() <= H.TOL
 
 
-def test_split_invariance(H):
+@pytest.mark.parametrize("layout", [0, 3])
+def test_split_invariance(H, layout):
+    """Any chunk size gives the oracle's result (the planner's head blocks,
+    and 64-head blocks)."""
     rng = np.random.default_rng(42)
     wl = WL.random_case(rng, rows=3, heads=64, D=512, block_size=64,
                         max_len=6000, width=2048, hole_frac=0.0, dup_frac=0.0,
                         oob_frac=0.0)
     outs = []
     for ct in (0, 64, 192, 512, 2048):
-        _announce("split", chunk=ct)
-        run = H.run_gpu(wl, chunk_tokens=ct, with_selection=False)
+        _announce("split", chunk=ct, layout=layout)
+        run = H.run_gpu(wl, chunk_tokens=ct, with_selection=False, layout=layout)
         outs.append(run.out)
     want = H.oracle_rows(wl, range(3))
     for o in outs:
@@ -493,12 +496,15 @@ def test_padded_page_stride(H):
     assert H.normwise_err(run.out, want).max() <= H.TOL
 
 
-def test_deterministic(H):
+@pytest.mark.parametrize("layout", [0, 3])
+def test_deterministic(H, layout):
+    """Two launches of the GLM workload give the same bits (the planner's
+    32-head blocks in four chunks, and 64-head blocks in eight)."""
     wl = WL.make("glm")
-    _announce("determinism")
+    _announce("determinism", layout=layout)
     pool = H.u8(wl.pool)
-    a = H.run_gpu(wl, k_pool=pool, with_selection=False)
-    b = H.run_gpu(wl, k_pool=pool, with_selection=False)
+    a = H.run_gpu(wl, k_pool=pool, with_selection=False, layout=layout)
+    b = H.run_gpu(wl, k_pool=pool, with_selection=False, layout=layout)
     assert np.array_equal(a.out_bits, b.out_bits)
 
 
